@@ -1,1 +1,164 @@
-"""fp4q: MI355X-native FP4 compression of tensor-parallel communication."""
+"""fp4q: MI355X-native FP4 compression of tensor-parallel communication.
+
+Thin ctypes binding over ``libfp4q.so`` (C ABI in ``include/fp4q.h``): the
+functions below carry the C entry points' names and only marshal arguments --
+torch tensors in, device pointers and the current HIP stream out.  Every step
+of the transform runs in the library's HIP kernels; there is no fallback, and
+a missing library raises.
+
+Method: "FP4Quant: Efficient 4-Bit Communication Compression for Model-Parallel
+LLM Training" (abstract).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4q.so")
+
+FP4Q_BLOCK = 256
+FP4Q_GROUP = 16
+FP4Q_MAX_PEERS = 16
+FP4Q_OUT_F32 = 0
+FP4Q_OUT_BF16 = 1
+FP4Q_FLAG_NO_FWHT = 1
+FP4Q_OK = 0
+FP4Q_ERR_NULL = 1
+FP4Q_ERR_SHAPE = 2
+FP4Q_ERR_ALIGN = 3
+FP4Q_ERR_K = 4
+FP4Q_ERR_ARG = 5
+FP4Q_ERR_LAUNCH = 6
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__("fp4q: %s (status %d)" % (fp4q_status_str(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("fp4q: %s is missing; build it with __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, U32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
+        PP = ctypes.POINTER(ctypes.c_void_p)
+        SZ = ctypes.POINTER(ctypes.c_size_t)
+        L.fp4q_payload_bytes.argtypes = [I64, I64, SZ, SZ, SZ]
+        L.fp4q_compress.argtypes = [P, I64, I64, P, P, P, P]
+        L.fp4q_compress_ex.argtypes = [P, I64, I64, P, P, P, U32, P]
+        L.fp4q_decompress.argtypes = [P, P, P, I64, I64, P, P]
+        L.fp4q_decompress_ex.argtypes = [P, P, P, I64, I64, P, I, U32, P]
+        L.fp4q_decompress_accumulate.argtypes = [I, PP, PP, PP, I64, I64, P, I, P]
+        L.fp4q_decompress_accumulate_ex.argtypes = [I, PP, PP, PP, I64, I64, P, I, U32, P]
+        L.fp4q_status_str.argtypes = [I]
+        L.fp4q_status_str.restype = ctypes.c_char_p
+        for f in ("fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex", "fp4q_decompress",
+                  "fp4q_decompress_ex", "fp4q_decompress_accumulate",
+                  "fp4q_decompress_accumulate_ex"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def fp4q_status_str(status: int) -> str:
+    return lib().fp4q_status_str(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != FP4Q_OK:
+        raise Fp4qError(status)
+
+
+def fp4q_payload_bytes(rows: int, row_len: int):
+    c, m, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().fp4q_payload_bytes(rows, row_len, ctypes.byref(c), ctypes.byref(m),
+                                    ctypes.byref(b)))
+    return c.value, m.value, b.value
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dims(x):
+    if x.dim() != 2:
+        raise ValueError("fp4q: expected a 2-D tensor [rows, row_len]")
+    if not x.is_contiguous():
+        raise ValueError("fp4q: expected a contiguous tensor")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def fp4q_compress(x, codes=None, micro_scales=None, block_scales=None, flags: int = 0,
+                  stream=None):
+    """bf16 [rows, row_len] (CUDA) -> (codes u8 [rows, L/2], micro u8 [rows, L/16],
+    block f32 [rows, L/256]).  Output tensors are allocated when not given."""
+    import torch
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("fp4q_compress: input must hold bf16 bit patterns")
+    rows, L = _dims(x)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
+    if micro_scales is None:
+        micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
+    if block_scales is None:
+        block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
+    _check(lib().fp4q_compress_ex(_ptr(x), rows, L, _ptr(codes), _ptr(micro_scales),
+                                  _ptr(block_scales), flags, _stream(stream)))
+    return codes, micro_scales, block_scales
+
+
+def _out_dtype_code(dtype):
+    import torch
+    if dtype == torch.float32:
+        return FP4Q_OUT_F32
+    if dtype == torch.bfloat16:
+        return FP4Q_OUT_BF16
+    raise TypeError("fp4q: output dtype must be float32 or bfloat16")
+
+
+def fp4q_decompress(codes, micro_scales, block_scales, out=None, out_dtype=None, flags: int = 0,
+                    stream=None):
+    """Payload -> [rows, row_len] float32 (or bfloat16)."""
+    import torch
+    rows, half = _dims(codes)
+    L = 2 * half
+    if out is None:
+        out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
+    _check(lib().fp4q_decompress_ex(_ptr(codes), _ptr(micro_scales), _ptr(block_scales), rows, L,
+                                    _ptr(out), _out_dtype_code(out.dtype), flags, _stream(stream)))
+    return out
+
+
+def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 0, stream=None):
+    """Sum of k peers' payloads [(codes, micro, block), ...] -> float32 (or bf16)."""
+    import torch
+    k = len(payloads)
+    rows, half = _dims(payloads[0][0]) if k else (0, 0)
+    L = 2 * half
+    if out is None:
+        out = torch.empty((rows, L), dtype=out_dtype or torch.float32,
+                          device=payloads[0][0].device)
+    PA = ctypes.c_void_p * max(k, 1)
+    cs = PA(*[p[0].data_ptr() for p in payloads])
+    ms = PA(*[p[1].data_ptr() for p in payloads])
+    bs = PA(*[p[2].data_ptr() for p in payloads])
+    cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+    _check(lib().fp4q_decompress_accumulate_ex(k, cast(cs), cast(ms), cast(bs), rows, L,
+                                               _ptr(out), _out_dtype_code(out.dtype), flags,
+                                               _stream(stream)))
+    return out

@@ -1,0 +1,526 @@
+// fp4q.hip -- gfx950 kernels and the C ABI of the FP4 communication-compression
+// library (declared in include/fp4q.h).
+//
+// Method: "FP4Quant: Efficient 4-Bit Communication Compression for Model-Parallel
+// LLM Training" (abstract): a hybrid two-level fast Walsh-Hadamard transform,
+// micro-grouped dual-scale FP4 quantisation and cooperative FP4 packing on the
+// sender; dequantisation, the inverse transform and (zot.news digest, "Read it
+// as": the AllReduce of tensor parallelism) the sum of k peers on the receiver.
+//
+// Work mapping (one wavefront = 64 lanes = a tile of 16 blocks of 256):
+//   lane l handles block  p = l & 15  of the tile and quarter  q = l >> 4  of
+//   that block, i.e. elements [64 q, 64 q + 64): 128 contiguous bytes of bf16,
+//   loaded with eight 16-byte loads.  Index bits 0-5 of the block sit in the
+//   lane's 64 registers, bits 6-7 in lane bits 4-5.
+//   Transform (radix-2 stages in the order stride 1, 2, ..., 128):
+//     strides 1..32  butterflies between registers;
+//     stride 64      v_permlane16_swap exchanges lane bit 4 with register bit 4
+//                    (index bit 4, already transformed), then a register butterfly;
+//     stride 128     v_permlane32_swap exchanges lane bit 5 with register bit 5,
+//                    then a register butterfly.
+//   Afterwards a lane holds four whole micro-groups g = q + 4k (k = 0..3), so
+//   group maxima, scales, quantisation and packing stay in registers; two more
+//   swap rounds on the packed codes give each lane 32 contiguous code bytes.
+// No LDS, no MFMA: the work is streaming and the transform is butterflies.
+//
+// Numerics follow the method's fp32 operation order exactly (built with
+// -ffp-contract=off, IEEE division, fp32 denormals kept):
+//   * the transform runs on unscaled values z = 16 y; the 1/16 is folded into
+//     the block maximum and the reciprocal scale, which is exact for bfloat16
+//     inputs (every intermediate is a multiple of 2^-133, so scaling by 2^-4
+//     never rounds, and z * (r / 16) is the same real number as (z / 16) * r);
+//   * E4M3 micro-scales use the hardware RNE conversion after clamping to 448
+//     (the conversion itself turns values above 464 into NaN);
+//   * E2M1 codes use the hardware RNE conversion with scale 1 (its scale operand
+//     only applies a power of two), which saturates at 6 and keeps the sign.
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "fp4q.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerWG = 4;
+constexpr int kThreads = kWave * kWavesPerWG;
+constexpr int kTileBlocks = 16;                        // 256-blocks per wavefront
+constexpr int kBlocksPerWG = kTileBlocks * kWavesPerWG;  // 64
+
+struct Lane {
+    int q;        // quarter of the block held by this lane (lane bits 4-5)
+    int64_t b;    // flat block index
+    bool valid;
+};
+
+__device__ __forceinline__ Lane lane_map(int64_t nblocks) {
+    Lane L;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerWG + (threadIdx.x / kWave);
+    L.q = lane >> 4;
+    L.b = wave * kTileBlocks + (lane & 15);
+    L.valid = L.b < nblocks;
+    return L;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (byte selectors of
+// the conversion builtins must be compile-time constants).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
+__device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
+
+// Exchange lane bit 4 (odd/even 16-lane rows) with the register pair (a, b):
+// afterwards a holds, in row parity L, what lane parity 0 held in register L,
+// and b what lane parity 1 held in register L.
+__device__ __forceinline__ void swap16(unsigned &a, unsigned &b) {
+    auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+// The same for lane bit 5 (upper / lower 32 lanes).
+__device__ __forceinline__ void swap32(unsigned &a, unsigned &b) {
+    auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    unsigned x = as_u(a), y = as_u(b);
+    swap16(x, y);
+    a = as_f(x);
+    b = as_f(y);
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    unsigned x = as_u(a), y = as_u(b);
+    swap32(x, y);
+    a = as_f(x);
+    b = as_f(y);
+}
+
+// One radix-2 stage between registers j and j + H.
+template <int H>
+__device__ __forceinline__ void stage(float (&R)[64]) {
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        if ((j & H) == 0) {
+            const float a = R[j], b = R[j + H];
+            R[j] = a + b;
+            R[j + H] = a - b;
+        }
+}
+
+// Unnormalised 256-point Walsh-Hadamard transform of the four lanes that share a
+// block (see the mapping above).  On return register j = 16 k + i of quarter q
+// holds element 16 q + 64 k + i.
+__device__ __forceinline__ void fwht256_unscaled(float (&R)[64]) {
+    stage<1>(R);   // level 1: index bits 0-3
+    stage<2>(R);
+    stage<4>(R);
+    stage<8>(R);
+    stage<16>(R);  // level 2: index bits 4-7
+    stage<32>(R);
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        if ((j & 16) == 0) swap16(R[j], R[j | 16]);
+    stage<16>(R);  // index bit 6
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        if ((j & 32) == 0) swap32(R[j], R[j | 32]);
+    stage<32>(R);  // index bit 7
+}
+
+// Maximum of v over the four lanes of a block (lane bits 4 and 5).
+__device__ __forceinline__ float block_lane_max(float v) {
+    float a = v, b = v;
+    swap16(a, b);
+    v = fmaxf(a, b);
+    a = v;
+    b = v;
+    swap32(a, b);
+    return fmaxf(a, b);
+}
+
+// 4x4 transpose over (lane bits 4-5) x (register index bits 0-1) of four values.
+template <typename T>
+__device__ __forceinline__ void transpose4(T &x0, T &x1, T &x2, T &x3) {
+    swap16(x0, x1);
+    swap16(x2, x3);
+    swap32(x0, x2);
+    swap32(x1, x3);
+}
+
+__device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
+    unsigned a = as_u(lo), b = as_u(hi);
+    a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+    b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+    return a | b;
+}
+
+// ---------------------------------------------------------------- compress
+template <bool kFwht>
+__global__ __launch_bounds__(kThreads) void compress_kernel(
+    const uint4 *__restrict__ in, int64_t nblocks, uint4 *__restrict__ codes,
+    unsigned *__restrict__ micro, float *__restrict__ block) {
+    const Lane L = lane_map(nblocks);
+
+    uint4 d[8];
+    if (L.valid) {
+        const uint4 *src = in + L.b * 32 + L.q * 8;  // 8 bf16 per uint4
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = src[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    float R[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const unsigned w[4] = {d[i].x, d[i].y, d[i].z, d[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            R[8 * i + 2 * k] = as_f(w[k] << 16);
+            R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+        }
+    }
+    if constexpr (kFwht) fwht256_unscaled(R);
+
+    // Group maxima (register group k = j >> 4) and the block maximum.
+    float a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(R[16 * k + i]));
+        a[k] = kFwht ? m * 0.0625f : m;
+    }
+    const float A = block_lane_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+    const float s = A / 2688.0f;  // 6 * 448
+    const float d6 = 6.0f * s;
+
+    float t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
+    unsigned mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+    mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+
+    float inv[4];
+    static_for<4>([&](auto k) {
+        const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+        float r = (S == 0.0f) ? 0.0f : 1.0f / S;
+        r = fminf(r, FLT_MAX);
+        inv[k] = kFwht ? r * 0.0625f : r;
+    });
+
+    unsigned C[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const float r = inv[w >> 1];
+        unsigned c = 0;
+        static_for<4>([&](auto sel) {
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j] * r, R[j + 1] * r, 1.0f,
+                                                         decltype(sel)::value);
+        });
+        C[w] = c;
+    }
+
+    if constexpr (kFwht) {
+        // lane q holds groups q + 4k in register pair k; make it groups 4q .. 4q + 3
+        transpose4(C[0], C[2], C[4], C[6]);
+        transpose4(C[1], C[3], C[5], C[7]);
+        transpose4(t[0], t[1], t[2], t[3]);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+    }
+
+    if (L.valid) {
+        uint4 *dst = codes + L.b * 8 + L.q * 2;
+        dst[0] = make_uint4(C[0], C[1], C[2], C[3]);
+        dst[1] = make_uint4(C[4], C[5], C[6], C[7]);
+        micro[L.b * 4 + L.q] = mw;
+        if (L.q == 0) block[L.b] = s;
+    }
+}
+
+// --------------------------------------------------- dequantise one payload
+// Registers j = 0..63 of quarter q get E2M1(code) * S_g for elements 64 q + j;
+// with kFma the products are added into R (receiver-side sum).
+template <bool kFma>
+__device__ __forceinline__ void dequant(const Lane &L, const uint4 *__restrict__ codes,
+                                        const unsigned *__restrict__ micro,
+                                        const float *__restrict__ block, float (&R)[64]) {
+    uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0;
+    unsigned mw = 0;
+    float s = 0.0f;
+    if (L.valid) {
+        const uint4 *src = codes + L.b * 8 + L.q * 2;
+        c0 = src[0];
+        c1 = src[1];
+        mw = micro[L.b * 4 + L.q];
+        s = block[L.b];
+    }
+    const unsigned C[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float S[4];
+    static_for<4>([&](auto k) { S[k] = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value); });
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const float Sg = S[w >> 1];
+        static_for<4>([&](auto sel) {
+            const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], 1.0f, decltype(sel)::value);
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            if constexpr (kFma) {
+                R[j] = fmaf(f[0], Sg, R[j]);
+                R[j + 1] = fmaf(f[1], Sg, R[j + 1]);
+            } else {
+                R[j] = f[0] * Sg;
+                R[j + 1] = f[1] * Sg;
+            }
+        });
+    }
+}
+
+// Store the 64 values of a lane.  After the transform register j = 16 k + i of
+// quarter q is element 16 q + 64 k + i; without it, element 64 q + j.
+template <bool kFwht, bool kBf16>
+__device__ __forceinline__ void store_out(const Lane &L, void *__restrict__ out,
+                                          const float (&R)[64]) {
+    if (!L.valid) return;
+    if constexpr (kBf16) {
+        uint4 *o = reinterpret_cast<uint4 *>(out);  // 8 bf16 per uint4
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int j = 8 * v;
+            const int64_t e = kFwht ? L.b * 256 + 16 * L.q + 64 * (v >> 1) + 8 * (v & 1)
+                                    : L.b * 256 + 64 * L.q + j;
+            o[e / 8] = make_uint4(bf16_rne_pair(R[j], R[j + 1]), bf16_rne_pair(R[j + 2], R[j + 3]),
+                                  bf16_rne_pair(R[j + 4], R[j + 5]),
+                                  bf16_rne_pair(R[j + 6], R[j + 7]));
+        }
+    } else {
+        uint4 *o = reinterpret_cast<uint4 *>(out);  // 4 fp32 per uint4
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int j = 4 * v;
+            const int64_t e = kFwht ? L.b * 256 + 16 * L.q + 64 * (v >> 2) + 4 * (v & 3)
+                                    : L.b * 256 + 64 * L.q + j;
+            o[e / 4] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
+        }
+    }
+}
+
+// -------------------------------------------------------------- decompress
+template <bool kFwht, bool kBf16>
+__global__ __launch_bounds__(kThreads) void decompress_kernel(
+    const uint4 *__restrict__ codes, const unsigned *__restrict__ micro,
+    const float *__restrict__ block, int64_t nblocks, void *__restrict__ out) {
+    const Lane L = lane_map(nblocks);
+    float R[64];
+    dequant<false>(L, codes, micro, block, R);
+    if constexpr (kFwht) {
+        fwht256_unscaled(R);
+#pragma unroll
+        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+    }
+    store_out<kFwht, kBf16>(L, out, R);
+}
+
+// --------------------------------------------------- receiver-side reduce
+struct Peers {
+    const uint4 *codes[FP4Q_MAX_PEERS];
+    const unsigned *micro[FP4Q_MAX_PEERS];
+    const float *block[FP4Q_MAX_PEERS];
+};
+
+// Sum in the transform domain (the transform is linear), then one inverse
+// transform for all peers.
+template <bool kFwht, bool kBf16>
+__global__ __launch_bounds__(kThreads) void accumulate_kernel(Peers peers, int k,
+                                                               int64_t nblocks,
+                                                               void *__restrict__ out) {
+    const Lane L = lane_map(nblocks);
+    float R[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) R[j] = 0.0f;
+    for (int p = 0; p < k; ++p) dequant<true>(L, peers.codes[p], peers.micro[p], peers.block[p], R);
+    if constexpr (kFwht) {
+        fwht256_unscaled(R);
+#pragma unroll
+        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+    }
+    store_out<kFwht, kBf16>(L, out, R);
+}
+
+// ------------------------------------------------------------------- host
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+inline Range rng(const void *p, int64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Validates the shape; on success sets n (elements) and nb (blocks).
+int check_shape(int64_t rows, int64_t row_len, int64_t *n, int64_t *nb) {
+    if (rows < 0 || row_len <= 0 || row_len % FP4Q_BLOCK != 0) return FP4Q_ERR_SHAPE;
+    // fp32 output bytes = 4 * rows * row_len must fit in int64
+    if (rows > 0 && row_len > INT64_MAX / 4 / rows) return FP4Q_ERR_SHAPE;
+    *n = rows * row_len;
+    *nb = *n / FP4Q_BLOCK;
+    // grid: one workgroup per 64 blocks
+    if ((*nb + kBlocksPerWG - 1) / kBlocksPerWG > (int64_t)0x7FFFFFFF) return FP4Q_ERR_SHAPE;
+    return FP4Q_OK;
+}
+
+int launch(const void *fn, int64_t nb, void **args, void *stream) {
+    const dim3 grid((unsigned)((nb + kBlocksPerWG - 1) / kBlocksPerWG)), threads(kThreads);
+    const hipError_t e = hipLaunchKernel(fn, grid, threads, args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_LAUNCH;
+}
+
+int check_payload_ptrs(const void *codes, const void *micro, const void *block) {
+    if (!codes || !micro || !block) return FP4Q_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(micro, 4) || !aligned(block, 4)) return FP4Q_ERR_ALIGN;
+    return FP4Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4q_payload_bytes(int64_t rows, int64_t row_len, size_t *codes_bytes, size_t *micro_bytes,
+                       size_t *block_bytes) {
+    int64_t n, nb;
+    const int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (codes_bytes) *codes_bytes = (size_t)(n / 2);
+    if (micro_bytes) *micro_bytes = (size_t)(n / FP4Q_GROUP);
+    if (block_bytes) *block_bytes = (size_t)(nb * 4);
+    return FP4Q_OK;
+}
+
+int fp4q_compress_ex(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
+                     uint8_t *micro_scales, float *block_scales, uint32_t flags, void *stream) {
+    int64_t n, nb;
+    int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (flags & ~(uint32_t)FP4Q_FLAG_NO_FWHT) return FP4Q_ERR_ARG;
+    if (n == 0) return FP4Q_OK;
+    if (!in_bf16) return FP4Q_ERR_NULL;
+    if ((st = check_payload_ptrs(codes, micro_scales, block_scales)) != FP4Q_OK) return st;
+    if (!aligned(in_bf16, 16)) return FP4Q_ERR_ALIGN;
+    const Range in = rng(in_bf16, 2 * n), c = rng(codes, n / 2), m = rng(micro_scales, n / 16),
+                b = rng(block_scales, 4 * nb);
+    if (overlap(in, c) || overlap(in, m) || overlap(in, b) || overlap(c, m) || overlap(c, b) ||
+        overlap(m, b))
+        return FP4Q_ERR_ARG;
+    void *args[] = {&in_bf16, &nb, &codes, &micro_scales, &block_scales};
+    const void *fn = (flags & FP4Q_FLAG_NO_FWHT) ? (const void *)&compress_kernel<false>
+                                                 : (const void *)&compress_kernel<true>;
+    return launch(fn, nb, args, stream);
+}
+
+int fp4q_compress(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
+                  uint8_t *micro_scales, float *block_scales, void *stream) {
+    return fp4q_compress_ex(in_bf16, rows, row_len, codes, micro_scales, block_scales, 0u, stream);
+}
+
+int fp4q_decompress_ex(const uint8_t *codes, const uint8_t *micro_scales,
+                       const float *block_scales, int64_t rows, int64_t row_len, void *out,
+                       int out_dtype, uint32_t flags, void *stream) {
+    int64_t n, nb;
+    int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (flags & ~(uint32_t)FP4Q_FLAG_NO_FWHT) return FP4Q_ERR_ARG;
+    if (out_dtype != FP4Q_OUT_F32 && out_dtype != FP4Q_OUT_BF16) return FP4Q_ERR_ARG;
+    if (n == 0) return FP4Q_OK;
+    if ((st = check_payload_ptrs(codes, micro_scales, block_scales)) != FP4Q_OK) return st;
+    if (!out) return FP4Q_ERR_NULL;
+    if (!aligned(out, 16)) return FP4Q_ERR_ALIGN;
+    const Range o = rng(out, (out_dtype == FP4Q_OUT_F32 ? 4 : 2) * n);
+    if (overlap(o, rng(codes, n / 2)) || overlap(o, rng(micro_scales, n / 16)) ||
+        overlap(o, rng(block_scales, 4 * nb)))
+        return FP4Q_ERR_ARG;
+    void *args[] = {&codes, &micro_scales, &block_scales, &nb, &out};
+    const bool fw = !(flags & FP4Q_FLAG_NO_FWHT), bf = out_dtype == FP4Q_OUT_BF16;
+    const void *fn = fw ? (bf ? (const void *)&decompress_kernel<true, true>
+                              : (const void *)&decompress_kernel<true, false>)
+                        : (bf ? (const void *)&decompress_kernel<false, true>
+                              : (const void *)&decompress_kernel<false, false>);
+    return launch(fn, nb, args, stream);
+}
+
+int fp4q_decompress(const uint8_t *codes, const uint8_t *micro_scales, const float *block_scales,
+                    int64_t rows, int64_t row_len, float *out_f32, void *stream) {
+    return fp4q_decompress_ex(codes, micro_scales, block_scales, rows, row_len, out_f32,
+                              FP4Q_OUT_F32, 0u, stream);
+}
+
+int fp4q_decompress_accumulate_ex(int k, const uint8_t *const *codes,
+                                  const uint8_t *const *micro_scales,
+                                  const float *const *block_scales, int64_t rows,
+                                  int64_t row_len, void *out, int out_dtype, uint32_t flags,
+                                  void *stream) {
+    int64_t n, nb;
+    int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (k < 1 || k > FP4Q_MAX_PEERS) return FP4Q_ERR_K;
+    if (flags & ~(uint32_t)FP4Q_FLAG_NO_FWHT) return FP4Q_ERR_ARG;
+    if (out_dtype != FP4Q_OUT_F32 && out_dtype != FP4Q_OUT_BF16) return FP4Q_ERR_ARG;
+    if (n == 0) return FP4Q_OK;
+    if (!codes || !micro_scales || !block_scales || !out) return FP4Q_ERR_NULL;
+    if (!aligned(out, 16)) return FP4Q_ERR_ALIGN;
+    const Range o = rng(out, (out_dtype == FP4Q_OUT_F32 ? 4 : 2) * n);
+    Peers peers = {};
+    for (int p = 0; p < k; ++p) {
+        if ((st = check_payload_ptrs(codes[p], micro_scales[p], block_scales[p])) != FP4Q_OK)
+            return st;
+        if (overlap(o, rng(codes[p], n / 2)) || overlap(o, rng(micro_scales[p], n / 16)) ||
+            overlap(o, rng(block_scales[p], 4 * nb)))
+            return FP4Q_ERR_ARG;
+        peers.codes[p] = reinterpret_cast<const uint4 *>(codes[p]);
+        peers.micro[p] = reinterpret_cast<const unsigned *>(micro_scales[p]);
+        peers.block[p] = block_scales[p];
+    }
+    void *args[] = {&peers, &k, &nb, &out};
+    const bool fw = !(flags & FP4Q_FLAG_NO_FWHT), bf = out_dtype == FP4Q_OUT_BF16;
+    const void *fn = fw ? (bf ? (const void *)&accumulate_kernel<true, true>
+                              : (const void *)&accumulate_kernel<true, false>)
+                        : (bf ? (const void *)&accumulate_kernel<false, true>
+                              : (const void *)&accumulate_kernel<false, false>);
+    return launch(fn, nb, args, stream);
+}
+
+int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,
+                               const uint8_t *const *micro_scales,
+                               const float *const *block_scales, int64_t rows, int64_t row_len,
+                               void *out, int out_dtype, void *stream) {
+    return fp4q_decompress_accumulate_ex(k, codes, micro_scales, block_scales, rows, row_len, out,
+                                         out_dtype, 0u, stream);
+}
+
+const char *fp4q_status_str(int status) {
+    switch (status) {
+        case FP4Q_OK: return "ok";
+        case FP4Q_ERR_NULL: return "null pointer";
+        case FP4Q_ERR_SHAPE: return "bad shape (rows >= 0, row_len > 0 and a multiple of 256)";
+        case FP4Q_ERR_ALIGN: return "misaligned pointer (16 bytes; 4 for scales)";
+        case FP4Q_ERR_K: return "peer count outside 1..16";
+        case FP4Q_ERR_ARG: return "bad flags, output type, or overlapping buffers";
+        case FP4Q_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+/*
+ * fp4q.h -- C ABI of the MI355X (gfx950) FP4 communication-compression library.
+ *
+ * The operations are those of "FP4Quant: Efficient 4-Bit Communication
+ * Compression for Model-Parallel LLM Training" (abstract): a bf16 tensor that a
+ * tensor-parallel rank is about to exchange is transformed block by block by a
+ * two-level fast Walsh-Hadamard transform, quantised to FP4 with two scales (one
+ * per block, one per micro-group of 16) and packed two codes per byte (zot.news
+ * digest of the same paper); the receiver dequantises, undoes the transform and
+ * sums the payloads of its k peers, the reduce of the tensor-parallel AllReduce
+ * (zot.news digest, "Read it as").
+ *
+ * Tensor: bf16, row-major [rows x row_len], row_len a multiple of 256.  Block b
+ * is the flat elements [256 b, 256 b + 256); a block never straddles a row.
+ * Payload of a tensor of N = rows * row_len elements, three flat arrays in block
+ * order:
+ *   codes        N/2 bytes; byte k = code[2k] | code[2k+1] << 4 (E2M1 codes:
+ *                sign | 2-bit exponent | 1-bit mantissa, values 0..6)
+ *   micro_scales N/16 bytes, OCP E4M3FN, one per 16 consecutive elements
+ *   block_scales N/256 fp32, one per block
+ * 4.625 bits per element.
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers; the caller allocates every buffer
+ *     and keeps ownership.  The library allocates nothing and keeps no state.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns as soon as the kernel is queued.  Device faults show up
+ *     at the caller's next synchronisation.
+ *   - Inputs are only read; outputs are fully overwritten.  Inputs and outputs
+ *     must not overlap (checked: FP4Q_ERR_ARG).
+ *   - Arguments are validated on the host before any HIP call, in this order:
+ *     shape (FP4Q_ERR_SHAPE: rows < 0, row_len <= 0, row_len % 256 != 0, or a
+ *     byte count that overflows int64), k (FP4Q_ERR_K), flags and out_dtype
+ *     (FP4Q_ERR_ARG), then pointers (FP4Q_ERR_NULL), alignment
+ *     (FP4Q_ERR_ALIGN), overlap (FP4Q_ERR_ARG).  rows == 0 returns FP4Q_OK
+ *     before the pointer checks and launches nothing.
+ *   - Alignment: bf16 input, codes and outputs 16 bytes; micro_scales and
+ *     block_scales 4 bytes.
+ *   - A failed launch returns FP4Q_ERR_LAUNCH.
+ *   - Inputs must be finite with |x| < 2^118; this is not checked.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { FP4Q_BLOCK = 256, FP4Q_GROUP = 16, FP4Q_MAX_PEERS = 16 };
+enum { FP4Q_OUT_F32 = 0, FP4Q_OUT_BF16 = 1 };
+/* Skip the Walsh-Hadamard transform on both sides (to measure what it buys). */
+enum { FP4Q_FLAG_NO_FWHT = 1u << 0 };
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_ERR_NULL = 1,
+    FP4Q_ERR_SHAPE = 2,
+    FP4Q_ERR_ALIGN = 3,
+    FP4Q_ERR_K = 4,
+    FP4Q_ERR_ARG = 5,
+    FP4Q_ERR_LAUNCH = 6
+} fp4q_status;
+
+/* Host-only helper: byte sizes of the three payload arrays for a tensor.
+ * Any of the output pointers may be NULL.  Returns FP4Q_OK or FP4Q_ERR_SHAPE. */
+int fp4q_payload_bytes(int64_t rows, int64_t row_len, size_t *codes_bytes,
+                       size_t *micro_bytes, size_t *block_bytes);
+
+/* Sender side ([FP4Quant] abstract: FWHT, micro-grouped dual-scale FP4
+ * quantisation, packing).  Per 256-block: y = H x / 16 (natural-order
+ * Walsh-Hadamard, radix-2 stages of stride 1, 2, ..., 128 in fp32);
+ * s = max|y| / 2688; per group g of 16: m_g = E4M3(max|y|_g / (6 s)) (round to
+ * nearest even, saturating at 448; s == 0 gives m_g = 0); S_g = s * m_g;
+ * code_i = E2M1(y_i * (1 / S_g)) (round to nearest even, saturating at 6, sign
+ * kept; a zero S_g has reciprocal 0, an overflowing one is clamped to FLT_MAX).
+ *   in_bf16       [rows x row_len] bf16 bit patterns
+ *   codes         N/2 bytes out;  micro_scales N/16 bytes out;  block_scales N/256 fp32 out */
+int fp4q_compress(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
+                  uint8_t *micro_scales, float *block_scales, void *stream);
+
+/* fp4q_compress with flags (0 or FP4Q_FLAG_NO_FWHT). */
+int fp4q_compress_ex(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
+                     uint8_t *micro_scales, float *block_scales, uint32_t flags, void *stream);
+
+/* Receiver side, one payload: yhat_i = E2M1(code_i) * S_g with S_g = s * m_g
+ * (fp32, as in compress), then the same transform (H / 16 is its own inverse),
+ * same fp32 operation order.  out_f32: [rows x row_len] fp32. */
+int fp4q_decompress(const uint8_t *codes, const uint8_t *micro_scales,
+                    const float *block_scales, int64_t rows, int64_t row_len, float *out_f32,
+                    void *stream);
+
+/* fp4q_decompress with an output type (FP4Q_OUT_F32, or FP4Q_OUT_BF16 rounded to
+ * nearest even) and flags (0 or FP4Q_FLAG_NO_FWHT). */
+int fp4q_decompress_ex(const uint8_t *codes, const uint8_t *micro_scales,
+                       const float *block_scales, int64_t rows, int64_t row_len, void *out,
+                       int out_dtype, uint32_t flags, void *stream);
+
+/* Receiver-side reduce of a tensor-parallel AllReduce (zot.news digest, "Read it
+ * as"): out = sum over p < k of decompress(payload p), all payloads of the same
+ * shape.  `codes`, `micro_scales` and `block_scales` are HOST arrays of k
+ * DEVICE pointers (copied into the kernel arguments; the arrays may be freed
+ * when the call returns).  1 <= k <= FP4Q_MAX_PEERS.  `out` is overwritten with
+ * the sum, fp32 or bf16 (out_dtype).  The sum is taken in fp32 in the transform
+ * domain (one inverse transform for all peers), so it matches an exact sum to
+ * about 1e-7 of the row's largest value, not bit for bit. */
+int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,
+                               const uint8_t *const *micro_scales,
+                               const float *const *block_scales, int64_t rows,
+                               int64_t row_len, void *out, int out_dtype, void *stream);
+
+/* fp4q_decompress_accumulate with flags (0 or FP4Q_FLAG_NO_FWHT). */
+int fp4q_decompress_accumulate_ex(int k, const uint8_t *const *codes,
+                                  const uint8_t *const *micro_scales,
+                                  const float *const *block_scales, int64_t rows,
+                                  int64_t row_len, void *out, int out_dtype, uint32_t flags,
+                                  void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *fp4q_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4Q_H */

@@ -1,0 +1,170 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Compress: block scales bit-exact; micro-scales and codes bit-exact except within
+1e-6 of a rounding boundary (tests/parity.py).  Decompress, fed the oracle's
+payload: bit-exact fp32 (and the 1e-6 row rule).  Receiver-side reduce: within
+1e-6 of the row maximum of the fp64 oracle sum."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from fp4_communication_compression_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fp4q():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import fp4_communication_compression_amd as m
+    m.lib()  # raises if the HIP library is missing: no fallback
+    oracle.set_threads(16)
+    return m
+
+
+DEV = "cuda:0"
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def gpu_compress(fp4q, xb, flags=0):
+    c, m, b = fp4q.fp4q_compress(to_dev(xb), flags=flags)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), m.cpu().numpy(), b.cpu().numpy()
+
+
+def run_compress_decompress(fp4q, xb, fwht=True, name=""):
+    _say("case %s shape %s fwht %s" % (name, xb.shape, fwht))
+    flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+    ref = oracle.compress(xb, fwht=fwht, debug=True)
+    got = gpu_compress(fp4q, xb, flags)
+    stats = parity.check_compress(got, ref)
+    # decompress the ORACLE payload on the GPU: equal codes -> bit-exact output
+    dp = [to_dev(ref[k]) for k in ("codes", "micro", "block")]
+    out = fp4q.fp4q_decompress(*dp, flags=flags)
+    out_bf = fp4q.fp4q_decompress(*dp, out_dtype=torch.bfloat16, flags=flags)
+    torch.cuda.synchronize()
+    want = oracle.decompress(ref["codes"], ref["micro"], ref["block"], fwht=fwht)
+    o = out.cpu().numpy()
+    np.testing.assert_array_equal(o.view(np.uint32), want.view(np.uint32))
+    parity.check_rowwise(o, want)
+    ob = out_bf.cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ob, inputs.f32_to_bf16_bits(want))
+    return stats
+
+
+SMALL = [("tiny", lambda: inputs.make_config("tiny")),
+         ("one_block", lambda: inputs.make_normal(1, 256, seed=3)),
+         ("ragged_37x4096", lambda: inputs.make_normal(37, 4096, seed=4, scale=2.0)),
+         ("mlp_5x11008", lambda: inputs.make_normal(5, 11008, seed=5)),
+         ("act_rows_100", lambda: inputs.make_config("act2048", rows=100)),
+         ("outlier_rows_100", lambda: inputs.make_config("outlier8192", rows=100))]
+EDGE = ["zeros", "ones", "spike", "tiny", "huge", "sparse", "ties", "mixed_blocks"]
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+@pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(fp4q, name, make, fwht):
+    st = run_compress_decompress(fp4q, make(), fwht, name)
+    assert st["code_mismatch"] == 0 and st["micro_mismatch"] == 0
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+@pytest.mark.parametrize("kind", EDGE)
+def test_edge_cases(fp4q, kind, fwht):
+    xb = inputs.make_edge_case(kind, 24, 1024, seed=9)
+    run_compress_decompress(fp4q, xb, fwht, "edge-" + kind)
+
+
+def test_empty_tensor(fp4q):
+    x = torch.empty((0, 4096), dtype=torch.bfloat16, device=DEV)
+    c, m, b = fp4q.fp4q_compress(x)
+    out = fp4q.fp4q_decompress(c, m, b)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4096)
+
+
+@pytest.mark.parametrize("name", ["act2048", "outlier8192", "large32768"])
+def test_full_size_configs(fp4q, name):
+    xb = inputs.make_config(name)
+    st = run_compress_decompress(fp4q, xb, True, name)
+    _say("  %s: %s" % (name, st))
+    if name in ("act2048", "outlier8192"):
+        run_compress_decompress(fp4q, xb, False, name + "-nofwht")
+
+
+def test_determinism(fp4q):
+    xb = inputs.make_config("act2048", rows=512)
+    x = to_dev(xb)
+    first = [t.clone() for t in fp4q.fp4q_compress(x)]
+    for _ in range(4):
+        again = fp4q.fp4q_compress(x)
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    out0 = fp4q.fp4q_decompress(*first)
+    for _ in range(3):
+        assert torch.equal(out0, fp4q.fp4q_decompress(*first))
+
+
+def _reduce_case(fp4q, peers_b, out_dtype=torch.float32, fwht=True):
+    ref = [oracle.compress(p, fwht=fwht) for p in peers_b]
+    trip = [(r["codes"], r["micro"], r["block"]) for r in ref]
+    want = oracle.accumulate_f64(trip, fwht=fwht)
+    dev = [tuple(to_dev(a) for a in t) for t in trip]
+    flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+    out = fp4q.fp4q_decompress_accumulate(dev, out_dtype=out_dtype, flags=flags)
+    torch.cuda.synchronize()
+    return out, want
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 8, 16])
+def test_reduce_small(fp4q, k):
+    _say("reduce small k=%d" % k)
+    peers = [inputs.make_normal(9, 2048, seed=50 + p, scale=1e-3) for p in range(k)]
+    out, want = _reduce_case(fp4q, peers)
+    parity.check_rowwise(out.cpu().numpy(), want)
+
+
+def test_reduce_nofwht_and_bf16(fp4q):
+    peers = [inputs.make_normal(7, 1280, seed=70 + p) for p in range(4)]
+    out, want = _reduce_case(fp4q, peers, fwht=False)
+    parity.check_rowwise(out.cpu().numpy(), want)
+    out, want = _reduce_case(fp4q, peers, out_dtype=torch.bfloat16)
+    o = out.float().cpu().numpy()
+    # bf16 output: within half a bf16 ulp (2^-9 relative) plus the fp32 sum error
+    err = np.abs(o - want).max(axis=1)
+    assert np.all(err <= (2.0 ** -8) * np.abs(want).max(axis=1))
+
+
+def test_reduce_full_size(fp4q):
+    """k = 8 payloads of 4096 x 11008, N(0, 1e-3), seeds 4..11 -> fp32."""
+    _say("reduce full k=8 4096x11008")
+    peers = [inputs.make_reduce_peer(p) for p in range(8)]
+    out, want = _reduce_case(fp4q, peers)
+    worst = parity.check_rowwise(out.cpu().numpy(), want)
+    _say("  worst row error / row max = %.3e" % worst)
+
+
+def test_roundtrip_rmse_matches_oracle(fp4q):
+    xb = inputs.make_config("act2048", rows=256)
+    x = to_dev(xb)
+    out = fp4q.fp4q_decompress(*fp4q.fp4q_compress(x))
+    torch.cuda.synchronize()
+    p = oracle.compress(xb)
+    ref = oracle.decompress(p["codes"], p["micro"], p["block"])
+    assert oracle.rel_rmse(xb, out.cpu().numpy()) == oracle.rel_rmse(xb, ref)
