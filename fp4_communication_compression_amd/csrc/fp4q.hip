@@ -7,21 +7,24 @@
 // sender; dequantisation, the inverse transform and (zot.news digest, "Read it
 // as": the AllReduce of tensor parallelism) the sum of k peers on the receiver.
 //
-// Work mapping (one wavefront = 64 lanes = a tile of 16 blocks of 256):
-//   lane l handles block  p = l & 15  of the tile and quarter  q = l >> 4  of
-//   that block, i.e. elements [64 q, 64 q + 64): 128 contiguous bytes of bf16,
-//   loaded with eight 16-byte loads.  Index bits 0-5 of the block sit in the
-//   lane's 64 registers, bits 6-7 in lane bits 4-5.
-//   Transform (radix-2 stages in the order stride 1, 2, ..., 128):
-//     strides 1..32  butterflies between registers;
-//     stride 64      v_permlane16_swap exchanges lane bit 4 with register bit 4
-//                    (index bit 4, already transformed), then a register butterfly;
-//     stride 128     v_permlane32_swap exchanges lane bit 5 with register bit 5,
-//                    then a register butterfly.
-//   Afterwards a lane holds four whole micro-groups g = q + 4k (k = 0..3), so
-//   group maxima, scales, quantisation and packing stay in registers; two more
-//   swap rounds on the packed codes give each lane 32 contiguous code bytes.
-// No LDS, no MFMA: the work is streaming and the transform is butterflies.
+// Work mapping: one wavefront (64 lanes) handles a tile of 16 blocks of 256
+// elements; lane l works on block p = l & 15 of the tile, together with the
+// lanes l ^ 16, l ^ 32, l ^ 48 ("quarters" q = l >> 4).  Each lane keeps 64
+// elements of its block in registers: six of the eight index bits of the block
+// are register-index bits, the other two are lane bits 4 and 5 (= q).
+//
+// Transform: radix-2 stages in the order stride 1, 2, ..., 128 (index bit 0 to
+// 7).  A stage on a register bit is a butterfly between two registers.  An index
+// bit that sits in a lane bit is first exchanged with an already transformed
+// register bit by v_permlane16_swap (lane bit 4) or v_permlane32_swap (lane bit
+// 5), one instruction per register pair, and then transformed in registers.
+// The order of these exchanges is chosen per kernel so that
+//   * every 16-byte global access of the four quarters covers whole 64-byte
+//     segments (loads use the non-temporal path; stores are only full-rate when
+//     an instruction writes whole segments),
+//   * compress ends with four whole micro-groups per lane, so group maxima,
+//     scales, quantisation and packing stay in registers.
+// No LDS and no MFMA: the work is streaming and the transform is butterflies.
 //
 // Numerics follow the method's fp32 operation order exactly (built with
 // -ffp-contract=off, IEEE division, fp32 denormals kept):
@@ -29,6 +32,10 @@
 //     the block maximum and the reciprocal scale, which is exact for bfloat16
 //     inputs (every intermediate is a multiple of 2^-133, so scaling by 2^-4
 //     never rounds, and z * (r / 16) is the same real number as (z / 16) * r);
+//   * divisions use a hardware reciprocal estimate refined by fused
+//     multiply-adds to the correctly rounded result; blocks whose largest
+//     transformed value is below 2^-80 (where a remainder could underflow) take
+//     the IEEE division instead;
 //   * E4M3 micro-scales use the hardware RNE conversion after clamping to 448
 //     (the conversion itself turns values above 464 into NaN);
 //   * E2M1 codes use the hardware RNE conversion with scale 1 (its scale operand
@@ -78,6 +85,14 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load on the non-temporal path (no allocation in the last-level cache).
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
 __device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
 
@@ -120,24 +135,33 @@ __device__ __forceinline__ void stage(float (&R)[64]) {
         }
 }
 
-// Unnormalised 256-point Walsh-Hadamard transform of the four lanes that share a
-// block (see the mapping above).  On return register j = 16 k + i of quarter q
-// holds element 16 q + 64 k + i.
-__device__ __forceinline__ void fwht256_unscaled(float (&R)[64]) {
-    stage<1>(R);   // level 1: index bits 0-3
-    stage<2>(R);
-    stage<4>(R);
-    stage<8>(R);
-    stage<16>(R);  // level 2: index bits 4-7
-    stage<32>(R);
+// Exchange lane bit 4 (resp. 5) with register-index bit H, for all 32 pairs.
+template <int H>
+__device__ __forceinline__ void swap_lane4(float (&R)[64]) {
 #pragma unroll
     for (int j = 0; j < 64; ++j)
-        if ((j & 16) == 0) swap16(R[j], R[j | 16]);
-    stage<16>(R);  // index bit 6
+        if ((j & H) == 0) swap16(R[j], R[j | H]);
+}
+template <int H>
+__device__ __forceinline__ void swap_lane5(float (&R)[64]) {
 #pragma unroll
     for (int j = 0; j < 64; ++j)
-        if ((j & 32) == 0) swap32(R[j], R[j | 32]);
-    stage<32>(R);  // index bit 7
+        if ((j & H) == 0) swap32(R[j], R[j | H]);
+}
+
+// Correctly rounded 1/x for 2^-125 <= |x| < 2^125: hardware estimate and one
+// Newton step (checked against IEEE division for every fp32 in that range).
+__device__ __forceinline__ float rcp_rn(float x) {
+    const float y = __builtin_amdgcn_rcpf(x);
+    const float e = fmaf(-x, y, 1.0f);
+    return fmaf(e, y, y);
+}
+// a / b rounded to nearest from y = rcp_rn(b) with one remainder correction;
+// the remainder a - q b is exact for a >= 2^-99 and normal b.
+__device__ __forceinline__ float div_rn(float a, float b, float y) {
+    const float q = a * y;
+    const float r = fmaf(-q, b, a);
+    return fmaf(r, y, q);
 }
 
 // Maximum of v over the four lanes of a block (lane bits 4 and 5).
@@ -168,6 +192,33 @@ __device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- compress
+// Loads: instruction j of quarter q reads 16-byte chunk q + 4 j of its block
+// (elements 8 (q + 4 j) .. + 7), so the four quarters read 64 contiguous bytes
+// per instruction.  Register j' = 8 j + t then holds index bits 0-2 = t and 5-7 =
+// j; lane bits 4, 5 hold index bits 3, 4.  After the transform's exchanges
+// register 16 k + i holds element 16 (b4 + 2 b5) + 64 k + i with lane bits 4, 5
+// = index bits 4, 5: quarter q owns micro-groups q, q + 4, q + 8, q + 12.
+// Without the transform the same exchanges are made (without butterflies).
+template <bool kFwht>
+__device__ __forceinline__ void compress_transform(float (&R)[64]) {
+    if constexpr (kFwht) {
+        stage<1>(R);       // index bit 0
+        stage<2>(R);       // 1
+        stage<4>(R);       // 2
+    }
+    swap_lane4<8>(R);      // register bit 3 <-> lane bit 4: index bit 3 in, 5 out
+    if constexpr (kFwht) stage<8>(R);   // 3
+    swap_lane5<16>(R);     // register bit 4 <-> lane bit 5: index bit 4 in, 6 out
+    if constexpr (kFwht) stage<16>(R);  // 4
+    swap_lane4<16>(R);     // register bit 4 <-> lane bit 4: index bit 5 in, 4 out
+    if constexpr (kFwht) stage<16>(R);  // 5
+    swap_lane5<16>(R);     // register bit 4 <-> lane bit 5: index bit 6 in, 5 out
+    if constexpr (kFwht) {
+        stage<16>(R);      // 6
+        stage<32>(R);      // 7 (register bit 5 since the load)
+    }
+}
+
 template <bool kFwht>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const uint4 *__restrict__ in, int64_t nblocks, uint4 *__restrict__ codes,
@@ -176,25 +227,25 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 
     uint4 d[8];
     if (L.valid) {
-        const uint4 *src = in + L.b * 32 + L.q * 8;  // 8 bf16 per uint4
+        const uint4 *src = in + L.b * 32 + L.q;  // 8 bf16 per uint4
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d[i] = src[i];
+        for (int j = 0; j < 8; ++j) d[j] = load_nt(src + 4 * j);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < 8; ++j) d[j] = make_uint4(0u, 0u, 0u, 0u);
     }
 
     float R[64];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const unsigned w[4] = {d[i].x, d[i].y, d[i].z, d[i].w};
+    for (int j = 0; j < 8; ++j) {
+        const unsigned w[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            R[8 * i + 2 * k] = as_f(w[k] << 16);
-            R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+            R[8 * j + 2 * k] = as_f(w[k] << 16);              // bf16 -> fp32, exact
+            R[8 * j + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
         }
     }
-    if constexpr (kFwht) fwht256_unscaled(R);
+    compress_transform<kFwht>(R);
 
     // Group maxima (register group k = j >> 4) and the block maximum.
     float a[4];
@@ -206,22 +257,38 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         a[k] = kFwht ? m * 0.0625f : m;
     }
     const float A = block_lane_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
-    const float s = A / 2688.0f;  // 6 * 448
-    const float d6 = 6.0f * s;
 
-    float t[4];
+    // Scales: s = A / 2688, t_k = a_k / (6 s), S_k = s E4M3(t_k), r_k = 1 / S_k.
+    float s, t[4], inv[4];
+    unsigned mw;
+    if (A >= 0x1p-80f) {
+        s = div_rn(A, 2688.0f, 1.0f / 2688.0f);
+        const float d6 = 6.0f * s;
+        const float y = rcp_rn(d6);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
-    unsigned mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-    mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
-
-    float inv[4];
-    static_for<4>([&](auto k) {
-        const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
-        float r = (S == 0.0f) ? 0.0f : 1.0f / S;
-        r = fminf(r, FLT_MAX);
-        inv[k] = kFwht ? r * 0.0625f : r;
-    });
+        for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), 448.0f);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+        static_for<4>([&](auto k) {
+            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+            inv[k] = (S == 0.0f) ? 0.0f : rcp_rn(S);
+        });
+    } else {  // tiny or zero block: IEEE division throughout
+        s = A / 2688.0f;
+        const float d6 = 6.0f * s;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+        static_for<4>([&](auto k) {
+            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+            inv[k] = fminf((S == 0.0f) ? 0.0f : 1.0f / S, FLT_MAX);
+        });
+    }
+    if constexpr (kFwht) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) inv[k] *= 0.0625f;  // exact: the folded 1/16
+    }
 
     unsigned C[8];
 #pragma unroll
@@ -236,44 +303,58 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         C[w] = c;
     }
 
-    if constexpr (kFwht) {
-        // lane q holds groups q + 4k in register pair k; make it groups 4q .. 4q + 3
-        transpose4(C[0], C[2], C[4], C[6]);
-        transpose4(C[1], C[3], C[5], C[7]);
-        transpose4(t[0], t[1], t[2], t[3]);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
-    }
+    // Code dword w of quarter q holds elements 8 e .. 8 e + 7 with index bits
+    // (3, 6, 7) = bits of w and (4, 5) = bits of q.  Re-deal the dwords so that q
+    // holds index bits 5, 6 and w bits (3, 4, 7): then the four quarters' 16-byte
+    // stores cover 64 contiguous bytes.
+    swap32(C[0], C[2]);  // lane bit 5 (index bit 5) <-> dword bit 1 (index bit 6)
+    swap32(C[1], C[3]);
+    swap32(C[4], C[6]);
+    swap32(C[5], C[7]);
+    swap16(C[0], C[2]);  // lane bit 4 (index bit 4) <-> dword bit 1 (index bit 5)
+    swap16(C[1], C[3]);
+    swap16(C[4], C[6]);
+    swap16(C[5], C[7]);
+    // micro-scales: quarter q holds groups q + 4k; make it groups 4q .. 4q + 3
+    transpose4(t[0], t[1], t[2], t[3]);
+    mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+    mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
 
     if (L.valid) {
-        uint4 *dst = codes + L.b * 8 + L.q * 2;
-        dst[0] = make_uint4(C[0], C[1], C[2], C[3]);
-        dst[1] = make_uint4(C[4], C[5], C[6], C[7]);
+        codes[L.b * 8 + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
+        codes[L.b * 8 + 4 + L.q] = make_uint4(C[4], C[5], C[6], C[7]);
         micro[L.b * 4 + L.q] = mw;
         if (L.q == 0) block[L.b] = s;
     }
 }
 
-// --------------------------------------------------- dequantise one payload
-// Registers j = 0..63 of quarter q get E2M1(code) * S_g for elements 64 q + j;
-// with kFma the products are added into R (receiver-side sum).
+// --------------------------------------------------- receiver: one payload
+// Loads: instruction h of quarter q reads code chunk q + 4 h (16 bytes = 32
+// codes), so the four quarters read 64 contiguous bytes per instruction.
+// Register j = 32 h + 8 w + t holds element 32 q + 128 h + 8 w + t: register
+// bits 0-4 = index bits 0-4, bit 5 = index bit 7; lane bits 4, 5 = index bits
+// 5, 6.  Its micro-group is (j >> 4 & 1) + 2 q + 8 h, so register group j >> 4
+// uses micro byte 2 q + (j >> 4 & 1) + 8 (j >> 5).
+// With kFma the dequantised values are added into R (receiver-side sum).
 template <bool kFma>
 __device__ __forceinline__ void dequant(const Lane &L, const uint4 *__restrict__ codes,
                                         const unsigned *__restrict__ micro,
                                         const float *__restrict__ block, float (&R)[64]) {
     uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0;
-    unsigned mw = 0;
+    unsigned lo = 0, hi = 0;
     float s = 0.0f;
     if (L.valid) {
-        const uint4 *src = codes + L.b * 8 + L.q * 2;
-        c0 = src[0];
-        c1 = src[1];
-        mw = micro[L.b * 4 + L.q];
+        const uint4 *src = codes + L.b * 8 + L.q;
+        c0 = load_nt(src);
+        c1 = load_nt(src + 4);
+        const unsigned sh = 16u * (L.q & 1);
+        lo = micro[L.b * 4 + (L.q >> 1)] >> sh;      // bytes 2q, 2q + 1
+        hi = micro[L.b * 4 + 2 + (L.q >> 1)] >> sh;  // bytes 2q + 8, 2q + 9
         s = block[L.b];
     }
     const unsigned C[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    float S[4];
-    static_for<4>([&](auto k) { S[k] = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value); });
+    const float S[4] = {s * __builtin_amdgcn_cvt_f32_fp8(lo, 0), s * __builtin_amdgcn_cvt_f32_fp8(lo, 1),
+                        s * __builtin_amdgcn_cvt_f32_fp8(hi, 0), s * __builtin_amdgcn_cvt_f32_fp8(hi, 1)};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const float Sg = S[w >> 1];
@@ -291,36 +372,61 @@ __device__ __forceinline__ void dequant(const Lane &L, const uint4 *__restrict__
     }
 }
 
-// Store the 64 values of a lane.  After the transform register j = 16 k + i of
-// quarter q is element 16 q + 64 k + i; without it, element 64 q + j.
+// Inverse transform (the same butterflies) and the output layout.  Index bits
+// 5 and 6 arrive in lane bits 4 and 5; they are exchanged with register bits
+// chosen so that the output's 16-byte stores cover whole 64-byte segments:
+//   fp32 out: with index bits 2, 3 -> register j of quarter q holds element
+//     (j & 3) + 4 q + 32 (j >> 2 & 1) + 64 (j >> 3 & 1) + 16 (j >> 4 & 1)
+//     + 128 (j >> 5);
+//   bf16 out: with index bits 3, 4 -> register j holds (j & 7) + 8 q + 32 (j >> 3).
+// Without the transform only the exchanges are made.
 template <bool kFwht, bool kBf16>
+__device__ __forceinline__ void receiver_transform(float (&R)[64]) {
+    constexpr int kA = kBf16 ? 8 : 4;    // register bit that takes index bit 5
+    constexpr int kB = kBf16 ? 16 : 8;   // register bit that takes index bit 6
+    if constexpr (kFwht) {
+        stage<1>(R);   // index bits 0-4
+        stage<2>(R);
+        stage<4>(R);
+        stage<8>(R);
+        stage<16>(R);
+    }
+    swap_lane4<kA>(R);
+    if constexpr (kFwht) stage<kA>(R);   // index bit 5
+    swap_lane5<kB>(R);
+    if constexpr (kFwht) {
+        stage<kB>(R);  // index bit 6
+        stage<32>(R);  // index bit 7
+#pragma unroll
+        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+    }
+}
+
+template <bool kBf16>
 __device__ __forceinline__ void store_out(const Lane &L, void *__restrict__ out,
                                           const float (&R)[64]) {
     if (!L.valid) return;
+    uint4 *o = reinterpret_cast<uint4 *>(out);
     if constexpr (kBf16) {
-        uint4 *o = reinterpret_cast<uint4 *>(out);  // 8 bf16 per uint4
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
+        for (int v = 0; v < 8; ++v) {  // 8 bf16 per uint4: registers 8v .. 8v + 7
             const int j = 8 * v;
-            const int64_t e = kFwht ? L.b * 256 + 16 * L.q + 64 * (v >> 1) + 8 * (v & 1)
-                                    : L.b * 256 + 64 * L.q + j;
+            const int64_t e = L.b * 256 + 8 * L.q + 32 * v;
             o[e / 8] = make_uint4(bf16_rne_pair(R[j], R[j + 1]), bf16_rne_pair(R[j + 2], R[j + 3]),
                                   bf16_rne_pair(R[j + 4], R[j + 5]),
                                   bf16_rne_pair(R[j + 6], R[j + 7]));
         }
     } else {
-        uint4 *o = reinterpret_cast<uint4 *>(out);  // 4 fp32 per uint4
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; ++v) {  // 4 fp32 per uint4: registers 4v .. 4v + 3
             const int j = 4 * v;
-            const int64_t e = kFwht ? L.b * 256 + 16 * L.q + 64 * (v >> 2) + 4 * (v & 3)
-                                    : L.b * 256 + 64 * L.q + j;
+            const int64_t e = L.b * 256 + 4 * L.q + 32 * (v & 1) + 64 * ((v >> 1) & 1) +
+                              16 * ((v >> 2) & 1) + 128 * (v >> 3);
             o[e / 4] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
         }
     }
 }
 
-// -------------------------------------------------------------- decompress
 template <bool kFwht, bool kBf16>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint4 *__restrict__ codes, const unsigned *__restrict__ micro,
@@ -328,12 +434,8 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const Lane L = lane_map(nblocks);
     float R[64];
     dequant<false>(L, codes, micro, block, R);
-    if constexpr (kFwht) {
-        fwht256_unscaled(R);
-#pragma unroll
-        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
-    }
-    store_out<kFwht, kBf16>(L, out, R);
+    receiver_transform<kFwht, kBf16>(R);
+    store_out<kBf16>(L, out, R);
 }
 
 // --------------------------------------------------- receiver-side reduce
@@ -354,12 +456,8 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(Peers peers, int k
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
     for (int p = 0; p < k; ++p) dequant<true>(L, peers.codes[p], peers.micro[p], peers.block[p], R);
-    if constexpr (kFwht) {
-        fwht256_unscaled(R);
-#pragma unroll
-        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
-    }
-    store_out<kFwht, kBf16>(L, out, R);
+    receiver_transform<kFwht, kBf16>(R);
+    store_out<kBf16>(L, out, R);
 }
 
 // ------------------------------------------------------------------- host
