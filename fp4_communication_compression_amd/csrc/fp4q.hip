@@ -53,24 +53,49 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerWG = 4;
-constexpr int kThreads = kWave * kWavesPerWG;
-constexpr int kTileBlocks = 16;                        // 256-blocks per wavefront
-constexpr int kBlocksPerWG = kTileBlocks * kWavesPerWG;  // 64
+constexpr int kTileBlocks = 16;  // 256-blocks per wavefront
+// Wavefronts per workgroup (all LDS use is per wavefront).  The compute-heavy
+// sender runs best with one wavefront per workgroup (more resident waves per
+// CU); the store-heavy receiver with four (neighbouring tiles write
+// neighbouring output from one CU).
+#ifndef FP4Q_SENDER_WAVES
+#define FP4Q_SENDER_WAVES 1
+#endif
+#ifndef FP4Q_RECEIVER_WAVES
+#define FP4Q_RECEIVER_WAVES 4
+#endif
+#ifndef FP4Q_RECEIVER_ROUND
+#define FP4Q_RECEIVER_ROUND 8
+#endif
+constexpr int kSenderWaves = FP4Q_SENDER_WAVES;
+constexpr int kReceiverWaves = FP4Q_RECEIVER_WAVES;
+// fp32 receiver output is staged kRoundBlocks blocks (65 chunks each) at a time
+constexpr int kRoundBlocks = FP4Q_RECEIVER_ROUND;
 
 struct Lane {
+    int lane;     // 0..63
+    int p;        // block within the tile (lane bits 0-3)
     int q;        // quarter of the block held by this lane (lane bits 4-5)
+    int64_t tile; // first block of the wavefront's tile (wave-uniform)
     int64_t b;    // flat block index
-    bool valid;
+    int64_t bl;   // block to load: b, clamped to the last block for idle lanes
+    bool valid;   // b < nblocks: only valid lanes store
 };
 
+// Lanes past the last block (a ragged final tile) load the last block instead
+// and compute on it without storing, so no branch or zero fill is needed before
+// the cross-lane exchanges (which need every lane).  nblocks >= 1.
+template <int kWaves>
 __device__ __forceinline__ Lane lane_map(int64_t nblocks) {
     Lane L;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerWG + (threadIdx.x / kWave);
-    L.q = lane >> 4;
-    L.b = wave * kTileBlocks + (lane & 15);
+    L.lane = threadIdx.x & (kWave - 1);
+    const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    L.tile = ((int64_t)blockIdx.x * kWaves + wave_in_wg) * kTileBlocks;
+    L.p = L.lane & 15;
+    L.q = L.lane >> 4;
+    L.b = L.tile + L.p;
     L.valid = L.b < nblocks;
+    L.bl = L.valid ? L.b : nblocks - 1;
     return L;
 }
 
@@ -91,6 +116,11 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// 16-byte store on the non-temporal path.
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
 }
 
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
@@ -191,68 +221,108 @@ __device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
     return a | b;
 }
 
+// Wave-private LDS staging: a wavefront exchanges data among its own lanes
+// through a region of 16-byte chunks (no workgroup barrier is needed; the
+// fences keep the compiler from reordering LDS accesses across the exchange).
+// Blocks are laid out with one chunk of padding (stride 33 chunks for 32 data
+// chunks, 65 for 64, 9 for 8), so that both the scattered and the contiguous
+// access patterns are free of bank conflicts and every address is a per-lane
+// base plus a constant.
+constexpr int kStageChunks = 528;  // 16 x 33 chunks = 8.25 KiB per wavefront
+// receiver: bf16 output needs 16 x 33 chunks, fp32 output kRoundBlocks x 65
+constexpr int kReceiverChunks = 65 * kRoundBlocks > 528 ? 65 * kRoundBlocks : 528;
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------- compress
-// Loads: instruction j of quarter q reads 16-byte chunk q + 4 j of its block
-// (elements 8 (q + 4 j) .. + 7), so the four quarters read 64 contiguous bytes
-// per instruction.  Register j' = 8 j + t then holds index bits 0-2 = t and 5-7 =
-// j; lane bits 4, 5 hold index bits 3, 4.  After the transform's exchanges
-// register 16 k + i holds element 16 (b4 + 2 b5) + 64 k + i with lane bits 4, 5
-// = index bits 4, 5: quarter q owns micro-groups q, q + 4, q + 8, q + 12.
-// Without the transform the same exchanges are made (without butterflies).
+// Input staging: the wavefront's tile (16 blocks of bf16, 8 KiB, contiguous)
+// is read with eight fully coalesced 1 KiB loads into the wave-private LDS
+// region, then each lane reads its 128 contiguous bytes: register j = element 64 q + j, i.e. register bits 0-5 =
+// index bits 0-5 and lane bits 4, 5 = index bits 6, 7.  After the transform's
+// two exchanges register 16 k + i holds element 16 q + 64 k + i: quarter q owns
+// micro-groups q, q + 4, q + 8, q + 12 (without the transform the same
+// exchanges are made, without butterflies).
 template <bool kFwht>
 __device__ __forceinline__ void compress_transform(float (&R)[64]) {
     if constexpr (kFwht) {
-        stage<1>(R);       // index bit 0
-        stage<2>(R);       // 1
-        stage<4>(R);       // 2
+        stage<1>(R);   // level 1: index bits 0-3
+        stage<2>(R);
+        stage<4>(R);
+        stage<8>(R);
+        stage<16>(R);  // level 2: index bits 4-7
+        stage<32>(R);
     }
-    swap_lane4<8>(R);      // register bit 3 <-> lane bit 4: index bit 3 in, 5 out
-    if constexpr (kFwht) stage<8>(R);   // 3
-    swap_lane5<16>(R);     // register bit 4 <-> lane bit 5: index bit 4 in, 6 out
-    if constexpr (kFwht) stage<16>(R);  // 4
-    swap_lane4<16>(R);     // register bit 4 <-> lane bit 4: index bit 5 in, 4 out
-    if constexpr (kFwht) stage<16>(R);  // 5
-    swap_lane5<16>(R);     // register bit 4 <-> lane bit 5: index bit 6 in, 5 out
-    if constexpr (kFwht) {
-        stage<16>(R);      // 6
-        stage<32>(R);      // 7 (register bit 5 since the load)
+    swap_lane4<16>(R);  // register bit 4 <-> lane bit 4: index bit 6 in, 4 out
+    if constexpr (kFwht) stage<16>(R);
+    swap_lane5<32>(R);  // register bit 5 <-> lane bit 5: index bit 7 in, 5 out
+    if constexpr (kFwht) stage<32>(R);
+}
+
+// Tile loads: instruction j reads chunk 64 j + lane of the tile = chunk
+// lane & 31 of block 2 j + (lane >> 5).  In a ragged last tile, blocks past the
+// end re-read the last block (never stored).
+__device__ __forceinline__ void load_tile(const uint4 *__restrict__ in, int64_t tile,
+                                          int64_t nblocks, int lane, uint4 (&d)[8]) {
+    if (tile + kTileBlocks <= nblocks) {
+        const uint4 *src = in + tile * 32 + lane;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = load_nt(src + 64 * j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int64_t blk = tile + 2 * j + (lane >> 5);
+            blk = blk < nblocks ? blk : nblocks - 1;
+            d[j] = load_nt(in + blk * 32 + (lane & 31));
+        }
     }
 }
 
 template <bool kFwht>
-__global__ __launch_bounds__(kThreads) void compress_kernel(
+__global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     const uint4 *__restrict__ in, int64_t nblocks, uint4 *__restrict__ codes,
     unsigned *__restrict__ micro, float *__restrict__ block) {
-    const Lane L = lane_map(nblocks);
+    __shared__ uint4 lds_all[kSenderWaves * kStageChunks];
+    const Lane L = lane_map<kSenderWaves>(nblocks);
+    uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
+    const int lane = L.lane, p = L.p, q = L.q;
+    const int64_t tile = L.tile;
 
-    uint4 d[8];
-    if (L.valid) {
-        const uint4 *src = in + L.b * 32 + L.q;  // 8 bf16 per uint4
+    // stage the tile through LDS; each lane then reads its 128 contiguous bytes
+    {
+        uint4 d[8];
+        load_tile(in, tile, nblocks, lane, d);
+        uint4 *dst = lds + 33 * (lane >> 5) + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) d[j] = load_nt(src + 4 * j);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d[j] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < 8; ++j) dst[66 * j] = d[j];
     }
-
+    wave_lds_sync();
     float R[64];
+    {
+        const uint4 *srcl = lds + 33 * p + 8 * q;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const unsigned w[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+        for (int i = 0; i < 8; ++i) {
+            const uint4 x = srcl[i];
+            const unsigned w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            R[8 * j + 2 * k] = as_f(w[k] << 16);              // bf16 -> fp32, exact
-            R[8 * j + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+            for (int k = 0; k < 4; ++k) {
+                R[8 * i + 2 * k] = as_f(w[k] << 16);              // bf16 -> fp32, exact
+                R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+            }
         }
     }
+
     compress_transform<kFwht>(R);
 
     // Group maxima (register group k = j >> 4) and the block maximum.
     float a[4];
-#pragma unroll
+    #pragma unroll
     for (int k = 0; k < 4; ++k) {
         float m = 0.0f;
-#pragma unroll
+    #pragma unroll
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(R[16 * k + i]));
         a[k] = kFwht ? m * 0.0625f : m;
     }
@@ -265,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         s = div_rn(A, 2688.0f, 1.0f / 2688.0f);
         const float d6 = 6.0f * s;
         const float y = rcp_rn(d6);
-#pragma unroll
+    #pragma unroll
         for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), 448.0f);
         mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
         mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
@@ -276,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     } else {  // tiny or zero block: IEEE division throughout
         s = A / 2688.0f;
         const float d6 = 6.0f * s;
-#pragma unroll
+    #pragma unroll
         for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
         mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
         mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
@@ -286,12 +356,12 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         });
     }
     if constexpr (kFwht) {
-#pragma unroll
+    #pragma unroll
         for (int k = 0; k < 4; ++k) inv[k] *= 0.0625f;  // exact: the folded 1/16
     }
 
     unsigned C[8];
-#pragma unroll
+    #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const float r = inv[w >> 1];
         unsigned c = 0;
@@ -305,8 +375,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 
     // Code dword w of quarter q holds elements 8 e .. 8 e + 7 with index bits
     // (3, 6, 7) = bits of w and (4, 5) = bits of q.  Re-deal the dwords so that q
-    // holds index bits 5, 6 and w bits (3, 4, 7): then the four quarters' 16-byte
-    // stores cover 64 contiguous bytes.
+    // holds index bits 5, 6 and w bits (3, 4, 7): 16-byte chunk q (dwords 0-3)
+    // and chunk q + 4 (dwords 4-7) of the block's 128 code bytes.
     swap32(C[0], C[2]);  // lane bit 5 (index bit 5) <-> dword bit 1 (index bit 6)
     swap32(C[1], C[3]);
     swap32(C[4], C[6]);
@@ -320,9 +390,22 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
     mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
 
+    // Codes through LDS (8 chunks per block, stride 9) so that the tile's 2 KiB
+    // of codes leave in two 1 KiB stores.
+    wave_lds_sync();  // every lane has read its input chunks
+    lds[9 * p + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
+    lds[9 * p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
+    wave_lds_sync();
+    {
+        const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
+    #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pb = 8 * u + (lane >> 3);
+            const uint4 v = srcl[72 * u];
+            if (tile + pb < nblocks) codes[(tile + pb) * 8 + (lane & 7)] = v;
+        }
+    }
     if (L.valid) {
-        codes[L.b * 8 + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
-        codes[L.b * 8 + 4 + L.q] = make_uint4(C[4], C[5], C[6], C[7]);
         micro[L.b * 4 + L.q] = mw;
         if (L.q == 0) block[L.b] = s;
     }
@@ -340,18 +423,13 @@ template <bool kFma>
 __device__ __forceinline__ void dequant(const Lane &L, const uint4 *__restrict__ codes,
                                         const unsigned *__restrict__ micro,
                                         const float *__restrict__ block, float (&R)[64]) {
-    uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0;
-    unsigned lo = 0, hi = 0;
-    float s = 0.0f;
-    if (L.valid) {
-        const uint4 *src = codes + L.b * 8 + L.q;
-        c0 = load_nt(src);
-        c1 = load_nt(src + 4);
-        const unsigned sh = 16u * (L.q & 1);
-        lo = micro[L.b * 4 + (L.q >> 1)] >> sh;      // bytes 2q, 2q + 1
-        hi = micro[L.b * 4 + 2 + (L.q >> 1)] >> sh;  // bytes 2q + 8, 2q + 9
-        s = block[L.b];
-    }
+    const uint4 *src = codes + L.bl * 8 + L.q;
+    const uint4 c0 = load_nt(src);
+    const uint4 c1 = load_nt(src + 4);
+    const unsigned sh = 16u * (L.q & 1);
+    const unsigned lo = micro[L.bl * 4 + (L.q >> 1)] >> sh;      // bytes 2q, 2q + 1
+    const unsigned hi = micro[L.bl * 4 + 2 + (L.q >> 1)] >> sh;  // bytes 2q + 8, 2q + 9
+    const float s = block[L.bl];
     const unsigned C[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const float S[4] = {s * __builtin_amdgcn_cvt_f32_fp8(lo, 0), s * __builtin_amdgcn_cvt_f32_fp8(lo, 1),
                         s * __builtin_amdgcn_cvt_f32_fp8(hi, 0), s * __builtin_amdgcn_cvt_f32_fp8(hi, 1)};
@@ -402,40 +480,72 @@ __device__ __forceinline__ void receiver_transform(float (&R)[64]) {
     }
 }
 
+// Output staging: every lane's values go through the wave-private LDS region so
+// that each global store instruction writes 1 KiB of contiguous output (64
+// lanes x 16 bytes), the pattern the memory system absorbs fastest; stores take
+// the non-temporal path.
 template <bool kBf16>
-__device__ __forceinline__ void store_out(const Lane &L, void *__restrict__ out,
-                                          const float (&R)[64]) {
-    if (!L.valid) return;
+__device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
+                                          void *__restrict__ out, const float (&R)[64]) {
+    const int lane = L.lane, p = L.p;
+    const int64_t tile = L.tile;
     uint4 *o = reinterpret_cast<uint4 *>(out);
     if constexpr (kBf16) {
+        // a block is 32 chunks of 8 bf16 (stride 33); register 8v + t is chunk q + 4v
+        uint4 *dst = lds + 33 * p + L.q;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {  // 8 bf16 per uint4: registers 8v .. 8v + 7
+        for (int v = 0; v < 8; ++v) {
             const int j = 8 * v;
-            const int64_t e = L.b * 256 + 8 * L.q + 32 * v;
-            o[e / 8] = make_uint4(bf16_rne_pair(R[j], R[j + 1]), bf16_rne_pair(R[j + 2], R[j + 3]),
-                                  bf16_rne_pair(R[j + 4], R[j + 5]),
-                                  bf16_rne_pair(R[j + 6], R[j + 7]));
+            dst[4 * v] = make_uint4(bf16_rne_pair(R[j], R[j + 1]), bf16_rne_pair(R[j + 2], R[j + 3]),
+                                    bf16_rne_pair(R[j + 4], R[j + 5]),
+                                    bf16_rne_pair(R[j + 6], R[j + 7]));
+        }
+        wave_lds_sync();
+        const uint4 *src = lds + 33 * (lane >> 5) + (lane & 31);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {  // blocks 2u, 2u + 1 of the tile
+            const int64_t blk = tile + 2 * u + (lane >> 5);
+            const uint4 v = src[66 * u];
+            if (blk < nblocks) store_nt(o + blk * 32 + (lane & 31), v);
         }
     } else {
+        // a block is 64 chunks of 4 fp32 (stride 65); register quad v holds chunk
+        // q + 8 (v & 1) + 16 (v >> 1 & 1) + 4 (v >> 2 & 1) + 32 (v >> 3).
+        // Rounds of kRoundBlocks blocks each.
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {  // 4 fp32 per uint4: registers 4v .. 4v + 3
-            const int j = 4 * v;
-            const int64_t e = L.b * 256 + 4 * L.q + 32 * (v & 1) + 64 * ((v >> 1) & 1) +
-                              16 * ((v >> 2) & 1) + 128 * (v >> 3);
-            o[e / 4] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
+        for (int h = 0; h < kTileBlocks / kRoundBlocks; ++h) {
+            if (p / kRoundBlocks == h) {
+                uint4 *dst = lds + 65 * (p % kRoundBlocks) + L.q;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int j = 4 * v;
+                    const int c = 8 * (v & 1) + 16 * ((v >> 1) & 1) + 4 * ((v >> 2) & 1) + 32 * (v >> 3);
+                    dst[c] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
+                }
+            }
+            wave_lds_sync();
+            const uint4 *src = lds + lane;
+#pragma unroll
+            for (int u = 0; u < kRoundBlocks; ++u) {
+                const int64_t blk = tile + kRoundBlocks * h + u;
+                const uint4 v = src[65 * u];
+                if (blk < nblocks) store_nt(o + blk * 64 + lane, v);
+            }
+            wave_lds_sync();
         }
     }
 }
 
 template <bool kFwht, bool kBf16>
-__global__ __launch_bounds__(kThreads) void decompress_kernel(
+__global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     const uint4 *__restrict__ codes, const unsigned *__restrict__ micro,
     const float *__restrict__ block, int64_t nblocks, void *__restrict__ out) {
-    const Lane L = lane_map(nblocks);
+    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
+    const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
     dequant<false>(L, codes, micro, block, R);
     receiver_transform<kFwht, kBf16>(R);
-    store_out<kBf16>(L, out, R);
+    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
 }
 
 // --------------------------------------------------- receiver-side reduce
@@ -448,16 +558,16 @@ struct Peers {
 // Sum in the transform domain (the transform is linear), then one inverse
 // transform for all peers.
 template <bool kFwht, bool kBf16>
-__global__ __launch_bounds__(kThreads) void accumulate_kernel(Peers peers, int k,
-                                                               int64_t nblocks,
-                                                               void *__restrict__ out) {
-    const Lane L = lane_map(nblocks);
+__global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
+    Peers peers, int k, int64_t nblocks, void *__restrict__ out) {
+    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
+    const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
     for (int p = 0; p < k; ++p) dequant<true>(L, peers.codes[p], peers.micro[p], peers.block[p], R);
     receiver_transform<kFwht, kBf16>(R);
-    store_out<kBf16>(L, out, R);
+    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
 }
 
 // ------------------------------------------------------------------- host
@@ -477,12 +587,13 @@ int check_shape(int64_t rows, int64_t row_len, int64_t *n, int64_t *nb) {
     *n = rows * row_len;
     *nb = *n / FP4Q_BLOCK;
     // grid: one workgroup per 64 blocks
-    if ((*nb + kBlocksPerWG - 1) / kBlocksPerWG > (int64_t)0x7FFFFFFF) return FP4Q_ERR_SHAPE;
+    if ((*nb + kTileBlocks - 1) / kTileBlocks > (int64_t)0x7FFFFFFF) return FP4Q_ERR_SHAPE;
     return FP4Q_OK;
 }
 
-int launch(const void *fn, int64_t nb, void **args, void *stream) {
-    const dim3 grid((unsigned)((nb + kBlocksPerWG - 1) / kBlocksPerWG)), threads(kThreads);
+int launch(const void *fn, int64_t nb, int waves, void **args, void *stream) {
+    const int64_t per_wg = (int64_t)kTileBlocks * waves;
+    const dim3 grid((unsigned)((nb + per_wg - 1) / per_wg)), threads(kWave * waves);
     const hipError_t e = hipLaunchKernel(fn, grid, threads, args, 0, (hipStream_t)stream);
     return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_LAUNCH;
 }
@@ -526,7 +637,7 @@ int fp4q_compress_ex(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uin
     void *args[] = {&in_bf16, &nb, &codes, &micro_scales, &block_scales};
     const void *fn = (flags & FP4Q_FLAG_NO_FWHT) ? (const void *)&compress_kernel<false>
                                                  : (const void *)&compress_kernel<true>;
-    return launch(fn, nb, args, stream);
+    return launch(fn, nb, kSenderWaves, args, stream);
 }
 
 int fp4q_compress(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
@@ -556,7 +667,7 @@ int fp4q_decompress_ex(const uint8_t *codes, const uint8_t *micro_scales,
                               : (const void *)&decompress_kernel<true, false>)
                         : (bf ? (const void *)&decompress_kernel<false, true>
                               : (const void *)&decompress_kernel<false, false>);
-    return launch(fn, nb, args, stream);
+    return launch(fn, nb, kReceiverWaves, args, stream);
 }
 
 int fp4q_decompress(const uint8_t *codes, const uint8_t *micro_scales, const float *block_scales,
@@ -597,7 +708,7 @@ int fp4q_decompress_accumulate_ex(int k, const uint8_t *const *codes,
                               : (const void *)&accumulate_kernel<true, false>)
                         : (bf ? (const void *)&accumulate_kernel<false, true>
                               : (const void *)&accumulate_kernel<false, false>);
-    return launch(fn, nb, args, stream);
+    return launch(fn, nb, kReceiverWaves, args, stream);
 }
 
 int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,
