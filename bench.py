@@ -18,8 +18,12 @@ cpu_baseline = the CPU oracle (compress + decompress) on a bounded sample of
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +34,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "compress+decompress GB/s of bf16 input and % HBM roofline, 32768x4096"
 PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "fp4_communication_compression_amd", "csrc", "fp4q.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_large32768.md")
+COPY_REF_BYTES = 256 << 20
+EVENT_EVERY = 8
 
 
 def log(*a):
@@ -40,6 +48,79 @@ def algorithmic_bytes(n: int):
     nb = n // 256
     payload = n // 2 + n // 16 + 4 * nb
     return {"compress": 2 * n + payload, "decompress": payload + 4 * n}
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m = re.search(r"traffic: source=(\w+) compress=(\d+) decompress=(\d+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    return {"compress": int(m.group(2)), "decompress": int(m.group(3))}
+
+
+def _short(kernel_name: str) -> str:
+    if "decompress_kernel" in kernel_name:
+        return "decompress"
+    if "compress_kernel" in kernel_name:
+        return "compress"
+    if "direct_copy_kernel" in kernel_name:
+        return "copy"
+    return kernel_name.split("(")[0][:40]
+
+
+def summarize_counters(fetch_dir: str, write_dir: str) -> str:
+    """Counter summary (markdown) from two rocprofv3 --pmc runs of this bench with
+    --copy-reference: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by what
+    the same counters read for a plain device copy of COPY_REF_BYTES."""
+    def load(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: float(np.median(v)) for k, v in vals.items()}
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    f_scale = COPY_REF_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = COPY_REF_BYTES / (write["copy"] * 1024.0)
+    n = 32768 * 4096
+    ab = algorithmic_bytes(n)
+    out = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) | algorithmic bytes | ratio |",
+           "|---|---|---|---|---|---|"]
+    traffic = {}
+    for k in ("compress", "decompress"):
+        t = fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale
+        traffic[k] = int(round(t))
+        out.append("| %s | %.0f | %.0f | %d | %d | %.3f |" % (k, fetch[k], write[k], traffic[k], ab[k], t / ab[k]))
+    out.append("| copy (%d B) | %.0f | %.0f | scale factors: fetch x%.3f, write x%.3f | | |"
+               % (COPY_REF_BYTES, fetch["copy"], write["copy"], f_scale, w_scale))
+    out.append("")
+    out.append("traffic: source=%s compress=%d decompress=%d" % (kernel_source_hash(), traffic["compress"],
+                                                                 traffic["decompress"]))
+    return "\n".join(out)
+
+
+def summarize_trace(trace_dir: str) -> str:
+    """Kernel durations from a rocprofv3 --kernel-trace --stats run (markdown)."""
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    out = ["| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = _short(r["Name"])
+        if name in ("compress", "decompress", "copy"):
+            m = re.search(r"((?:de)?compress_kernel<[^>]*>|direct_copy_kernel)", r["Name"])
+            out.append("| %s | %s | %.2f | %.2f | %.2f |" % (
+                m.group(1) if m else name, r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    return "\n".join(out)
 
 
 def cpu_baseline(xb: np.ndarray, target_s: float = 12.0):
@@ -66,11 +147,23 @@ def cpu_baseline(xb: np.ndarray, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="also run a plain %d-byte device copy (counter scale reference)" % COPY_REF_BYTES)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the kernel durations of a rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the method shards by block range "
               "with no halo; the multi-GPU exchange is not part of it); run with --gpus 1",
@@ -105,23 +198,35 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    if args.copy_reference:
+        src = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     log("warmup %d" % args.warmup)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # Per-kernel durations: HIP events on the launch stream around both kernels of
+    # every EVENT_EVERY-th step of the timed region (an event pair costs a few us
+    # of GPU time, so recording them on every step would slow the steps down).
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_c = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_d = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    log("timed %d steps: %.3f ms/step; compress %.1f us, decompress %.1f us (mean)" %
-        (K, wall / K * 1e3, t_c.mean() * 1e6, t_d.mean() * 1e6))
+    t_c = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e-3
+    t_d = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e-3
+    log("timed %d steps: %.3f ms/step; compress %.1f us, decompress %.1f us (mean of %d sampled steps)" %
+        (K, wall / K * 1e3, t_c.mean() * 1e6, t_d.mean() * 1e6, len(sampled)))
 
     ab = algorithmic_bytes(n)
     kern = {}
@@ -158,7 +263,8 @@ def main():
                                "(fp32 out) per step, 3 rotating buffer sets",
                    "rows": rows, "row_len": L, "block": 256, "micro_group": 16},
         "roofline": {"bound": "hbm", "achieved": kern[dom]["achieved_GBps"], "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": kern[dom]["frac"], "traffic": None,
+                     "unit": "GB/s", "frac": kern[dom]["frac"],
+                     "traffic": (measured_traffic() or {}).get(dom),
                      "kernel": dom},
         "kernels": kern,
         "combined_roofline_frac": round((ab["compress"] + ab["decompress"]) /
