@@ -118,9 +118,16 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 // 16-byte store on the non-temporal path.
+#ifndef FP4Q_RECEIVER_STORE_NT
+#define FP4Q_RECEIVER_STORE_NT 1
+#endif
 __device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
+#if FP4Q_RECEIVER_STORE_NT
     const u32x4 t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
+#else
+    *p = v;
+#endif
 }
 
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
@@ -419,20 +426,36 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
 // 5, 6.  Its micro-group is (j >> 4 & 1) + 2 q + 8 h, so register group j >> 4
 // uses micro byte 2 q + (j >> 4 & 1) + 8 (j >> 5).
 // With kFma the dequantised values are added into R (receiver-side sum).
-template <bool kFma>
-__device__ __forceinline__ void dequant(const Lane &L, const uint4 *__restrict__ codes,
-                                        const unsigned *__restrict__ micro,
-                                        const float *__restrict__ block, float (&R)[64]) {
+// One lane's part of a payload: 32 code bytes, two micro-scale pairs, the block scale.
+struct PayloadRegs {
+    uint4 c0, c1;
+    unsigned lo, hi;  // micro-scale bytes (2q, 2q + 1) and (2q + 8, 2q + 9) in the low halves
+    float s;
+};
+
+__device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *__restrict__ codes,
+                                                    const unsigned *__restrict__ micro,
+                                                    const float *__restrict__ block) {
+    PayloadRegs P;
     const uint4 *src = codes + L.bl * 8 + L.q;
-    const uint4 c0 = load_nt(src);
-    const uint4 c1 = load_nt(src + 4);
+    P.c0 = load_nt(src);
+    P.c1 = load_nt(src + 4);
     const unsigned sh = 16u * (L.q & 1);
-    const unsigned lo = micro[L.bl * 4 + (L.q >> 1)] >> sh;      // bytes 2q, 2q + 1
-    const unsigned hi = micro[L.bl * 4 + 2 + (L.q >> 1)] >> sh;  // bytes 2q + 8, 2q + 9
-    const float s = block[L.bl];
-    const unsigned C[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float S[4] = {s * __builtin_amdgcn_cvt_f32_fp8(lo, 0), s * __builtin_amdgcn_cvt_f32_fp8(lo, 1),
-                        s * __builtin_amdgcn_cvt_f32_fp8(hi, 0), s * __builtin_amdgcn_cvt_f32_fp8(hi, 1)};
+    P.lo = micro[L.bl * 4 + (L.q >> 1)] >> sh;
+    P.hi = micro[L.bl * 4 + 2 + (L.q >> 1)] >> sh;
+    P.s = block[L.bl];
+    return P;
+}
+
+// Registers j = 0..63 get E2M1(code) * S_g; with kFma the products are added
+// into R (receiver-side sum).
+template <bool kFma>
+__device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64]) {
+    const unsigned C[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
+    const float S[4] = {P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 0),
+                        P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 1),
+                        P.s * __builtin_amdgcn_cvt_f32_fp8(P.hi, 0),
+                        P.s * __builtin_amdgcn_cvt_f32_fp8(P.hi, 1)};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const float Sg = S[w >> 1];
@@ -543,7 +566,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
-    dequant<false>(L, codes, micro, block, R);
+    dequant<false>(load_payload(L, codes, micro, block), R);
     receiver_transform<kFwht, kBf16>(R);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
 }
@@ -565,7 +588,17 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
     float R[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
-    for (int p = 0; p < k; ++p) dequant<true>(L, peers.codes[p], peers.micro[p], peers.block[p], R);
+    // two payloads in flight: the next peer's loads are issued before the
+    // current peer is dequantised
+    PayloadRegs A = load_payload(L, peers.codes[0], peers.micro[0], peers.block[0]);
+    int p = 0;
+    for (; p + 2 <= k; p += 2) {
+        const PayloadRegs B = load_payload(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
+        dequant<true>(A, R);
+        if (p + 2 < k) A = load_payload(L, peers.codes[p + 2], peers.micro[p + 2], peers.block[p + 2]);
+        dequant<true>(B, R);
+    }
+    if (p < k) dequant<true>(A, R);
     receiver_transform<kFwht, kBf16>(R);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
 }
