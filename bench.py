@@ -123,6 +123,37 @@ def summarize_trace(trace_dir: str) -> str:
     return "\n".join(out)
 
 
+def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
+    """Throughput and relative RMSE with and without the transform on the activation
+    (2048x4096) and outlier (8192x4096) workloads.  These tensors fit in the 256 MB
+    last-level cache, so their rates are cache-resident, not HBM roofline figures."""
+    rows_out = []
+    for name in ("act2048", "outlier8192"):
+        xb = inputs.make_config(name)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        xf = x.double()
+        for flags, label in ((0, "fwht"), (fp4q.FP4Q_FLAG_NO_FWHT, "no_fwht")):
+            P = fp4q.fp4q_compress(x, flags=flags)
+            Y = fp4q.fp4q_decompress(*P, flags=flags)
+            for _ in range(5):
+                fp4q.fp4q_compress(x, *P, flags=flags)
+                fp4q.fp4q_decompress(*P, out=Y, flags=flags)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(iters):
+                fp4q.fp4q_compress(x, *P, flags=flags)
+                fp4q.fp4q_decompress(*P, out=Y, flags=flags)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / iters
+            rmse = float(torch.linalg.vector_norm(Y.double() - xf) / torch.linalg.vector_norm(xf))
+            rows_out.append({"workload": name, "transform": label, "us_per_step": round(dt * 1e6, 1),
+                             "GBps_bf16_in": round(2 * x.numel() / dt / 1e9, 1),
+                             "rel_rmse": round(rmse, 6)})
+            log("tradeoff %-12s %-8s %7.1f us  %7.1f GB/s  rel RMSE %.6f" % (
+                name, label, dt * 1e6, 2 * x.numel() / dt / 1e9, rmse))
+    return rows_out
+
+
 def cpu_baseline(xb: np.ndarray, target_s: float = 12.0):
     import oracle
     threads = min(16, os.cpu_count() or 1)
@@ -151,6 +182,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--tradeoff", action="store_true",
+                    help="also report throughput and error with and without the transform "
+                         "on the 2048x4096 and 8192x4096 workloads")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain %d-byte device copy (counter scale reference)" % COPY_REF_BYTES)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -280,6 +314,8 @@ def main():
                                         (t_c.mean() + t_d.mean()) / 1e9 / PEAK_GBPS, 4),
         "rel_rmse": {"fwht": round(rmse, 6), "no_fwht": round(rmse_nf, 6)},
     }
+    if args.tradeoff:
+        result["tradeoff"] = fwht_tradeoff(fp4q, inputs, torch, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(xb)
