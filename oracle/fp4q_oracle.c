@@ -159,14 +159,11 @@ void fp4q_ref_fwht256_f64(double *y) {
  *   S_g = s * E4M3value(m_g);  r_g = 1 / S_g, taken as 0 when S_g == 0 and as
  *         FLT_MAX when 1 / S_g overflows (S_g below 2^-128)
  *   v_i = y_i * r_g;  code_i = E2M1(v_i)
- *   byte k = code[2k] | code[2k+1] << 4 */
-static void compress_block(const uint16_t *x, int fwht, uint8_t *codes, uint8_t *micro,
-                           float *block, float *v_out, float *t_out) {
-    float y[BLOCK];
+ *   byte k = code[2k] | code[2k+1] << 4
+ * quantize_block performs every step after the transform. */
+static void quantize_block(const float *y, uint8_t *codes, uint8_t *micro, float *block,
+                           float *v_out, float *t_out) {
     uint8_t code[BLOCK];
-    for (int i = 0; i < BLOCK; ++i) y[i] = widen_bf16(x[i]);
-    if (fwht) fp4q_ref_fwht256(y);
-
     float A = 0.0f;
     for (int i = 0; i < BLOCK; ++i) A = fmaxf(A, fabsf(y[i]));
     float s = A / 2688.0f;
@@ -197,6 +194,14 @@ static void compress_block(const uint16_t *x, int fwht, uint8_t *codes, uint8_t 
     }
     for (int k = 0; k < BLOCK / 2; ++k)
         codes[k] = (uint8_t)(code[2 * k] | (code[2 * k + 1] << 4));
+}
+
+static void compress_block(const uint16_t *x, int fwht, uint8_t *codes, uint8_t *micro,
+                           float *block, float *v_out, float *t_out) {
+    float y[BLOCK];
+    for (int i = 0; i < BLOCK; ++i) y[i] = widen_bf16(x[i]);
+    if (fwht) fp4q_ref_fwht256(y);
+    quantize_block(y, codes, micro, block, v_out, t_out);
 }
 
 /* Flat block order: block b holds elements [256 b, 256 b + 256) of the row-major
@@ -272,6 +277,30 @@ void fp4q_ref_accumulate_f64(int k, const uint8_t *const *codes, const uint8_t *
             for (int i = 0; i < BLOCK; ++i) acc[i] += d[i];
         }
         memcpy(out + BLOCK * b, acc, sizeof acc);
+    }
+}
+
+/* Receiver step of a compressed AllReduce split into a reduce-scatter and an
+ * all-gather: the k payloads a rank receives for its slice are summed and the
+ * sum is quantised again for the all-gather.  Reading: the sum is taken where
+ * the payloads live, in the transform domain (decompressing k payloads, summing
+ * and compressing again would apply H/16 twice, and H/16 is its own inverse), in
+ * fp32, each term E2M1value(code) * S_g as in decompress, added in peer order
+ * p = 0 .. k-1 to an accumulator that starts at +0; then the quantisation
+ * steps of compress (block maximum onwards) apply to the sum. */
+void fp4q_ref_requantize(int k, const uint8_t *const *codes, const uint8_t *const *micro,
+                         const float *const *block, int64_t nblocks, uint8_t *out_codes,
+                         uint8_t *out_micro, float *out_block, float *v_out, float *t_out) {
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t b = 0; b < nblocks; ++b) {
+        float acc[BLOCK], d[BLOCK];
+        for (int i = 0; i < BLOCK; ++i) acc[i] = 0.0f;
+        for (int p = 0; p < k; ++p) {
+            decompress_block(codes[p] + (BLOCK / 2) * b, micro[p] + NGROUP * b, block[p][b], 0, d);
+            for (int i = 0; i < BLOCK; ++i) acc[i] = acc[i] + d[i];
+        }
+        quantize_block(acc, out_codes + (BLOCK / 2) * b, out_micro + NGROUP * b, out_block + b,
+                       v_out ? v_out + BLOCK * b : NULL, t_out ? t_out + NGROUP * b : NULL);
     }
 }
 
