@@ -58,11 +58,12 @@ def lib() -> ctypes.CDLL:
         L.fp4q_decompress_ex.argtypes = [P, P, P, I64, I64, P, I, U32, P]
         L.fp4q_decompress_accumulate.argtypes = [I, PP, PP, PP, I64, I64, P, I, P]
         L.fp4q_decompress_accumulate_ex.argtypes = [I, PP, PP, PP, I64, I64, P, I, U32, P]
+        L.fp4q_reduce_requantize.argtypes = [I, PP, PP, PP, I64, I64, P, P, P, P]
         L.fp4q_status_str.argtypes = [I]
         L.fp4q_status_str.restype = ctypes.c_char_p
         for f in ("fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex", "fp4q_decompress",
                   "fp4q_decompress_ex", "fp4q_decompress_accumulate",
-                  "fp4q_decompress_accumulate_ex"):
+                  "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -162,3 +163,28 @@ def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 
                                                _ptr(out), _out_dtype_code(out.dtype), flags,
                                                _stream(stream)))
     return out
+
+
+def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales=None,
+                           stream=None):
+    """Sum k peers' payloads [(codes, micro, block), ...] in the transform domain
+    and quantise the sum again -> (codes, micro, block) of the same shape."""
+    import torch
+    k = len(payloads)
+    rows, half = _dims(payloads[0][0]) if k else (0, 0)
+    L = 2 * half
+    dev = payloads[0][0].device
+    if codes is None:
+        codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
+    if micro_scales is None:
+        micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
+    if block_scales is None:
+        block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
+    PA = ctypes.c_void_p * max(k, 1)
+    cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+    cs = PA(*[p[0].data_ptr() for p in payloads])
+    ms = PA(*[p[1].data_ptr() for p in payloads])
+    bs = PA(*[p[2].data_ptr() for p in payloads])
+    _check(lib().fp4q_reduce_requantize(k, cast(cs), cast(ms), cast(bs), rows, L, _ptr(codes),
+                                        _ptr(micro_scales), _ptr(block_scales), _stream(stream)))
+    return codes, micro_scales, block_scales

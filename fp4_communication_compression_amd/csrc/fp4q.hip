@@ -269,6 +269,87 @@ __device__ __forceinline__ void compress_transform(float (&R)[64]) {
     if constexpr (kFwht) stage<32>(R);
 }
 
+// Scales and codes of the four register groups of a lane (registers
+// 16 k .. 16 k + 15 form micro-group k; the four lanes of a block hold its 16
+// groups).  kScaled: the registers hold 16 y (the transform's 1/16 not yet
+// applied), which is folded into the block maximum and the reciprocals.
+//   s  = max|y| / 2688 over the block;  t_k = max|y|_k / (6 s), clamped to 448;
+//   mw = the four E4M3 micro-scales (byte k);  C = eight dwords of packed codes
+//        (dword w covers registers 8 w .. 8 w + 7, low nibble first).
+template <bool kScaled>
+__device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, float (&t)[4],
+                                                unsigned &mw, unsigned (&C)[8]) {
+    float a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(R[16 * k + i]));
+        a[k] = kScaled ? m * 0.0625f : m;
+    }
+    const float A = block_lane_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+
+    float inv[4];
+    if (A >= 0x1p-80f) {
+        s = div_rn(A, 2688.0f, 1.0f / 2688.0f);
+        const float d6 = 6.0f * s;
+        const float y = rcp_rn(d6);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), 448.0f);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+        static_for<4>([&](auto k) {
+            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+            inv[k] = (S == 0.0f) ? 0.0f : rcp_rn(S);
+        });
+    } else {  // tiny or zero block: IEEE division throughout
+        s = A / 2688.0f;
+        const float d6 = 6.0f * s;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+        static_for<4>([&](auto k) {
+            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+            inv[k] = fminf((S == 0.0f) ? 0.0f : 1.0f / S, FLT_MAX);
+        });
+    }
+    if constexpr (kScaled) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) inv[k] *= 0.0625f;  // exact: the folded 1/16
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const float r = inv[w >> 1];
+        unsigned c = 0;
+        static_for<4>([&](auto sel) {
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j] * r, R[j + 1] * r, 1.0f,
+                                                         decltype(sel)::value);
+        });
+        C[w] = c;
+    }
+}
+
+// Codes of a tile through LDS (8 chunks per block, stride 9): C[0..3] is the
+// lane's 16-byte chunk q of its block, C[4..7] chunk q + 4; the tile's 2 KiB of
+// codes then leave in two 1 KiB stores.  The caller has finished any earlier use
+// of the LDS region.
+__device__ __forceinline__ void store_codes(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
+                                            uint4 *__restrict__ codes, const unsigned (&C)[8]) {
+    const int lane = L.lane;
+    lds[9 * L.p + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
+    lds[9 * L.p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
+    wave_lds_sync();
+    const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t blk = L.tile + 8 * u + (lane >> 3);
+        const uint4 v = srcl[72 * u];
+        if (blk < nblocks) codes[blk * 8 + (lane & 7)] = v;
+    }
+}
+
 // Tile loads: instruction j reads chunk 64 j + lane of the tile = chunk
 // lane & 31 of block 2 j + (lane >> 5).  In a ragged last tile, blocks past the
 // end re-read the last block (never stored).
@@ -324,61 +405,9 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
 
     compress_transform<kFwht>(R);
 
-    // Group maxima (register group k = j >> 4) and the block maximum.
-    float a[4];
-    #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float m = 0.0f;
-    #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(R[16 * k + i]));
-        a[k] = kFwht ? m * 0.0625f : m;
-    }
-    const float A = block_lane_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
-
-    // Scales: s = A / 2688, t_k = a_k / (6 s), S_k = s E4M3(t_k), r_k = 1 / S_k.
-    float s, t[4], inv[4];
-    unsigned mw;
-    if (A >= 0x1p-80f) {
-        s = div_rn(A, 2688.0f, 1.0f / 2688.0f);
-        const float d6 = 6.0f * s;
-        const float y = rcp_rn(d6);
-    #pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), 448.0f);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
-        static_for<4>([&](auto k) {
-            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
-            inv[k] = (S == 0.0f) ? 0.0f : rcp_rn(S);
-        });
-    } else {  // tiny or zero block: IEEE division throughout
-        s = A / 2688.0f;
-        const float d6 = 6.0f * s;
-    #pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
-        static_for<4>([&](auto k) {
-            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
-            inv[k] = fminf((S == 0.0f) ? 0.0f : 1.0f / S, FLT_MAX);
-        });
-    }
-    if constexpr (kFwht) {
-    #pragma unroll
-        for (int k = 0; k < 4; ++k) inv[k] *= 0.0625f;  // exact: the folded 1/16
-    }
-
-    unsigned C[8];
-    #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        const float r = inv[w >> 1];
-        unsigned c = 0;
-        static_for<4>([&](auto sel) {
-            const int j = 8 * w + 2 * decltype(sel)::value;
-            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j] * r, R[j + 1] * r, 1.0f,
-                                                         decltype(sel)::value);
-        });
-        C[w] = c;
-    }
+    float s, t[4];
+    unsigned mw, C[8];
+    quantize_groups<kFwht>(R, s, t, mw, C);
 
     // Code dword w of quarter q holds elements 8 e .. 8 e + 7 with index bits
     // (3, 6, 7) = bits of w and (4, 5) = bits of q.  Re-deal the dwords so that q
@@ -397,21 +426,8 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
     mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
 
-    // Codes through LDS (8 chunks per block, stride 9) so that the tile's 2 KiB
-    // of codes leave in two 1 KiB stores.
     wave_lds_sync();  // every lane has read its input chunks
-    lds[9 * p + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
-    lds[9 * p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
-    wave_lds_sync();
-    {
-        const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
-    #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int pb = 8 * u + (lane >> 3);
-            const uint4 v = srcl[72 * u];
-            if (tile + pb < nblocks) codes[(tile + pb) * 8 + (lane & 7)] = v;
-        }
-    }
+    store_codes(L, nblocks, lds, codes, C);
     if (L.valid) {
         micro[L.b * 4 + L.q] = mw;
         if (L.q == 0) block[L.b] = s;
@@ -447,9 +463,11 @@ __device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *
     return P;
 }
 
-// Registers j = 0..63 get E2M1(code) * S_g; with kFma the products are added
-// into R (receiver-side sum).
-template <bool kFma>
+// Registers j = 0..63 get E2M1(code) * S_g (kSet), or the product is added to
+// them with one fused multiply-add (kFma) or as a rounded product and a rounded
+// sum (kAdd, the order the re-quantisation defines).
+enum DequantMode { kSet, kFma, kAdd };
+template <DequantMode kMode>
 __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64]) {
     const unsigned C[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
     const float S[4] = {P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 0),
@@ -462,9 +480,13 @@ __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64]) {
         static_for<4>([&](auto sel) {
             const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], 1.0f, decltype(sel)::value);
             const int j = 8 * w + 2 * decltype(sel)::value;
-            if constexpr (kFma) {
+            if constexpr (kMode == kFma) {
                 R[j] = fmaf(f[0], Sg, R[j]);
                 R[j + 1] = fmaf(f[1], Sg, R[j + 1]);
+            } else if constexpr (kMode == kAdd) {
+                const float p0 = f[0] * Sg, p1 = f[1] * Sg;  // built without contraction
+                R[j] = R[j] + p0;
+                R[j + 1] = R[j + 1] + p1;
             } else {
                 R[j] = f[0] * Sg;
                 R[j + 1] = f[1] * Sg;
@@ -566,7 +588,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
-    dequant<false>(load_payload(L, codes, micro, block), R);
+    dequant<kSet>(load_payload(L, codes, micro, block), R);
     receiver_transform<kFwht, kBf16>(R);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
 }
@@ -594,13 +616,52 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
     int p = 0;
     for (; p + 2 <= k; p += 2) {
         const PayloadRegs B = load_payload(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
-        dequant<true>(A, R);
+        dequant<kFma>(A, R);
         if (p + 2 < k) A = load_payload(L, peers.codes[p + 2], peers.micro[p + 2], peers.block[p + 2]);
-        dequant<true>(B, R);
+        dequant<kFma>(B, R);
     }
-    if (p < k) dequant<true>(A, R);
+    if (p < k) dequant<kFma>(A, R);
     receiver_transform<kFwht, kBf16>(R);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
+}
+
+
+// ------------------------------------------- receiver-side re-quantisation
+// Reduce-scatter step of a compressed AllReduce: the k payloads of a slice are
+// summed where they live, in the transform domain (rounded products added in
+// peer order to an accumulator that starts at +0), and the sum is quantised
+// again with the compress steps -- no transform is needed, since decompressing,
+// summing and compressing would apply the self-inverse H / 16 twice.
+// Register j of quarter q holds element 32 q + 128 (j >> 5) + (j & 31), so
+// register group k = j >> 4 is micro-group (k & 1) + 2 q + 8 (k >> 1), and code
+// dwords 0-3 / 4-7 are the block's 16-byte chunks q / q + 4.
+__global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
+    Peers peers, int k, int64_t nblocks, uint4 *__restrict__ codes,
+    unsigned short *__restrict__ micro, float *__restrict__ block) {
+    __shared__ uint4 lds[kReceiverWaves * 144];
+    const Lane L = lane_map<kReceiverWaves>(nblocks);
+    float R[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) R[j] = 0.0f;
+    PayloadRegs A = load_payload(L, peers.codes[0], peers.micro[0], peers.block[0]);
+    int p = 0;
+    for (; p + 2 <= k; p += 2) {
+        const PayloadRegs B = load_payload(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
+        dequant<kAdd>(A, R);
+        if (p + 2 < k) A = load_payload(L, peers.codes[p + 2], peers.micro[p + 2], peers.block[p + 2]);
+        dequant<kAdd>(B, R);
+    }
+    if (p < k) dequant<kAdd>(A, R);
+
+    float s, t[4];
+    unsigned mw, C[8];
+    quantize_groups<false>(R, s, t, mw, C);
+    store_codes(L, nblocks, lds + (threadIdx.x / kWave) * 144, codes, C);
+    if (L.valid) {
+        micro[L.b * 8 + L.q] = (unsigned short)(mw & 0xFFFFu);  // groups 2q, 2q + 1
+        micro[L.b * 8 + 4 + L.q] = (unsigned short)(mw >> 16);  // groups 2q + 8, 2q + 9
+        if (L.q == 0) block[L.b] = s;
+    }
 }
 
 // ------------------------------------------------------------------- host
@@ -750,6 +811,35 @@ int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,
                                void *out, int out_dtype, void *stream) {
     return fp4q_decompress_accumulate_ex(k, codes, micro_scales, block_scales, rows, row_len, out,
                                          out_dtype, 0u, stream);
+}
+
+int fp4q_reduce_requantize(int k, const uint8_t *const *codes, const uint8_t *const *micro_scales,
+                           const float *const *block_scales, int64_t rows, int64_t row_len,
+                           uint8_t *out_codes, uint8_t *out_micro, float *out_block,
+                           void *stream) {
+    int64_t n, nb;
+    int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (k < 1 || k > FP4Q_MAX_PEERS) return FP4Q_ERR_K;
+    if (n == 0) return FP4Q_OK;
+    if (!codes || !micro_scales || !block_scales) return FP4Q_ERR_NULL;
+    if ((st = check_payload_ptrs(out_codes, out_micro, out_block)) != FP4Q_OK) return st;
+    const Range oc = rng(out_codes, n / 2), om = rng(out_micro, n / 16), ob = rng(out_block, 4 * nb);
+    if (overlap(oc, om) || overlap(oc, ob) || overlap(om, ob)) return FP4Q_ERR_ARG;
+    Peers peers = {};
+    for (int p = 0; p < k; ++p) {
+        if ((st = check_payload_ptrs(codes[p], micro_scales[p], block_scales[p])) != FP4Q_OK)
+            return st;
+        const Range ic = rng(codes[p], n / 2), im = rng(micro_scales[p], n / 16),
+                    ib = rng(block_scales[p], 4 * nb);
+        for (const Range o : {oc, om, ob})
+            if (overlap(o, ic) || overlap(o, im) || overlap(o, ib)) return FP4Q_ERR_ARG;
+        peers.codes[p] = reinterpret_cast<const uint4 *>(codes[p]);
+        peers.micro[p] = reinterpret_cast<const unsigned *>(micro_scales[p]);
+        peers.block[p] = block_scales[p];
+    }
+    void *args[] = {&peers, &k, &nb, &out_codes, &out_micro, &out_block};
+    return launch((const void *)&requantize_kernel, nb, kReceiverWaves, args, stream);
 }
 
 const char *fp4q_status_str(int status) {

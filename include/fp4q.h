@@ -118,6 +118,27 @@ int fp4q_decompress_accumulate_ex(int k, const uint8_t *const *codes,
                                   int64_t row_len, void *out, int out_dtype, uint32_t flags,
                                   void *stream);
 
+/* Receiver step of a compressed AllReduce done as a reduce-scatter followed by
+ * an all-gather (the AllReduce of tensor parallelism, zot.news digest of
+ * [FP4Quant], "Read it as"): the k payloads a rank receives for its slice are
+ * summed and the sum is quantised again into one payload, ready for the
+ * all-gather.  The sum is taken in the transform domain -- each term
+ * E2M1(code) * S_g as in decompress, rounded products added in peer order to
+ * an accumulator that starts at +0, in fp32 -- and then quantised with the
+ * compress steps from the block maximum on; no transform is applied, because
+ * decompress + sum + compress would apply the self-inverse H / 16 twice.  The
+ * result therefore decompresses (with the same flags as its inputs) to the sum
+ * of the k decompressed tensors up to FP4 rounding.
+ *   codes, micro_scales, block_scales: HOST arrays of k DEVICE pointers (as in
+ *     fp4q_decompress_accumulate), 1 <= k <= FP4Q_MAX_PEERS
+ *   out_codes, out_micro, out_block: the new payload (same shape), must not
+ *     overlap any input. */
+int fp4q_reduce_requantize(int k, const uint8_t *const *codes,
+                           const uint8_t *const *micro_scales,
+                           const float *const *block_scales, int64_t rows, int64_t row_len,
+                           uint8_t *out_codes, uint8_t *out_micro, float *out_block,
+                           void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *fp4q_status_str(int status);
 

@@ -23,7 +23,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex",
                             "fp4q_decompress", "fp4q_decompress_ex", "fp4q_decompress_accumulate",
-                            "fp4q_decompress_accumulate_ex", "fp4q_status_str"])
+                            "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize",
+                            "fp4q_status_str"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -114,3 +115,26 @@ def test_accumulate_validation_order():
     assert acc(1, cs, ms, bs, 1, 256, out + 4) == fp4q.FP4Q_ERR_ALIGN
     assert acc(2, cs + [A + 4], ms * 2, bs * 2, 1, 256, out) == fp4q.FP4Q_ERR_ALIGN
     assert acc(1, [out + 16], ms, bs, 4, 256, out) == fp4q.FP4Q_ERR_ARG   # overlap with out
+
+
+def req(k, cs, ms, bs, rows, L, oc, om, ob):
+    PA = ctypes.c_void_p * max(len(cs), 1)
+    cast = lambda a: ctypes.cast(PA(*a), ctypes.POINTER(ctypes.c_void_p))
+    return fp4q.lib().fp4q_reduce_requantize(k, cast(cs), cast(ms), cast(bs), rows, L, oc, om, ob,
+                                             None)
+
+
+def test_requantize_validation_order():
+    big = 1 << 30
+    cs, ms, bs = [A], [A + big], [A + 2 * big]
+    outs = (A + 3 * big, A + 4 * big, A + 5 * big)
+    assert req(1, cs, ms, bs, 1, 200, *outs) == fp4q.FP4Q_ERR_SHAPE
+    assert req(0, cs, ms, bs, 1, 256, *outs) == fp4q.FP4Q_ERR_K
+    assert req(17, cs * 17, ms * 17, bs * 17, 1, 256, *outs) == fp4q.FP4Q_ERR_K
+    assert req(1, cs, ms, bs, 0, 256, *outs) == fp4q.FP4Q_OK
+    assert req(1, cs, ms, bs, 1, 256, NULL, outs[1], outs[2]) == fp4q.FP4Q_ERR_NULL
+    assert req(2, cs + [NULL], ms * 2, bs * 2, 1, 256, *outs) == fp4q.FP4Q_ERR_NULL
+    assert req(1, cs, ms, bs, 1, 256, outs[0] + 8, outs[1], outs[2]) == fp4q.FP4Q_ERR_ALIGN
+    assert req(1, cs, ms, bs, 1, 256, outs[0], outs[1] + 2, outs[2]) == fp4q.FP4Q_ERR_ALIGN
+    assert req(1, cs, ms, bs, 4, 256, A + 16, outs[1], outs[2]) == fp4q.FP4Q_ERR_ARG   # over input codes
+    assert req(1, cs, ms, bs, 4, 256, outs[0], outs[0] + 16, outs[2]) == fp4q.FP4Q_ERR_ARG

@@ -168,3 +168,38 @@ def test_roundtrip_rmse_matches_oracle(fp4q):
     p = oracle.compress(xb)
     ref = oracle.decompress(p["codes"], p["micro"], p["block"])
     assert oracle.rel_rmse(xb, out.cpu().numpy()) == oracle.rel_rmse(xb, ref)
+
+
+@pytest.mark.parametrize("k,rows,L", [(1, 4, 256), (2, 37, 4096), (3, 5, 11008), (8, 64, 4096),
+                                      (16, 9, 2048)])
+def test_requantize_parity(fp4q, k, rows, L):
+    _say("requantize k=%d %dx%d" % (k, rows, L))
+    peers = [inputs.make_normal(rows, L, seed=200 + p, scale=1e-3) for p in range(k)]
+    trip = [(r["codes"], r["micro"], r["block"]) for r in (oracle.compress(p) for p in peers)]
+    ref = oracle.requantize(trip, debug=True)
+    out = fp4q.fp4q_reduce_requantize([tuple(to_dev(a) for a in t) for t in trip])
+    torch.cuda.synchronize()
+    st = parity.check_compress([o.cpu().numpy() for o in out], ref)
+    assert st["code_mismatch"] == 0 and st["micro_mismatch"] == 0
+
+
+@pytest.mark.parametrize("kind", ["tiny", "huge", "mixed_blocks", "zeros"])
+def test_requantize_edge_cases(fp4q, kind):
+    peers = [inputs.make_edge_case(kind, 12, 1024, seed=300 + p) for p in range(3)]
+    trip = [(r["codes"], r["micro"], r["block"]) for r in (oracle.compress(p) for p in peers)]
+    ref = oracle.requantize(trip, debug=True)
+    out = fp4q.fp4q_reduce_requantize([tuple(to_dev(a) for a in t) for t in trip])
+    torch.cuda.synchronize()
+    parity.check_compress([o.cpu().numpy() for o in out], ref)
+
+
+def test_requantize_full_size(fp4q):
+    """k = 8 slices of 4096 x 11008 (the reduce workload)."""
+    _say("requantize full k=8 4096x11008")
+    peers = [inputs.make_reduce_peer(p) for p in range(8)]
+    trip = [(r["codes"], r["micro"], r["block"]) for r in (oracle.compress(p) for p in peers)]
+    ref = oracle.requantize(trip, debug=True)
+    out = fp4q.fp4q_reduce_requantize([tuple(to_dev(a) for a in t) for t in trip])
+    torch.cuda.synchronize()
+    st = parity.check_compress([o.cpu().numpy() for o in out], ref)
+    _say("  %s" % st)
