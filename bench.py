@@ -123,6 +123,45 @@ def summarize_trace(trace_dir: str) -> str:
     return "\n".join(out)
 
 
+def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
+    """The receiver's kernels on the reduce workload (k = 8 peers of 4096 x 11008,
+    N(0, 1e-3)): fp4q_decompress_accumulate (fp32 out) and fp4q_reduce_requantize.
+    Three rotating copies of the payloads; HIP events around every launch."""
+    k, rows, L = 8, 4096, 11008
+    n = rows * L
+    pay = []
+    for p in range(k):
+        xb = inputs.make_reduce_peer(p)
+        pay.append(fp4q.fp4q_compress(torch.from_numpy(xb.view(np.int16)).to(dev)))
+    sets = [pay] + [[tuple(t.clone() for t in q) for q in pay] for _ in range(2)]
+    out = [torch.empty((rows, L), dtype=torch.float32, device=dev) for _ in range(3)]
+    req = [fp4q.fp4q_reduce_requantize(pay) for _ in range(3)]
+    payload = n // 2 + n // 16 + n // 64
+    res = {}
+    for name, fn, nbytes in (
+            ("decompress_accumulate", lambda i: fp4q.fp4q_decompress_accumulate(sets[i % 3], out=out[i % 3]),
+             k * payload + 4 * n),
+            ("reduce_requantize", lambda i: fp4q.fp4q_reduce_requantize(sets[i % 3], *req[i % 3]),
+             (k + 1) * payload)):
+        for i in range(6):
+            fn(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        gbps = nbytes / t.mean() / 1e9
+        res[name] = {"avg_us": round(t.mean() * 1e6, 2), "algorithmic_bytes": nbytes,
+                     "achieved_GBps": round(gbps, 1), "frac": round(gbps / PEAK_GBPS, 4)}
+        log("receiver %-22s %7.1f us  %7.1f GB/s  %.1f%% of HBM peak" % (name, t.mean() * 1e6, gbps,
+                                                                        100 * gbps / PEAK_GBPS))
+    res["workload"] = "k=8 peers of bf16 4096x11008 N(0,1e-3), seeds 4..11"
+    return res
+
+
 def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
     """Throughput and relative RMSE with and without the transform on the activation
     (2048x4096) and outlier (8192x4096) workloads.  These tensors fit in the 256 MB
@@ -182,6 +221,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-receiver", action="store_true",
+                    help="skip the receiver-kernel timings on the k=8 reduce workload")
     ap.add_argument("--tradeoff", action="store_true",
                     help="also report throughput and error with and without the transform "
                          "on the 2048x4096 and 8192x4096 workloads")
@@ -310,10 +351,14 @@ def main():
                      "traffic": (measured_traffic() or {}).get(dom),
                      "kernel": dom},
         "kernels": kern,
+        # the whole step (compress + decompress) against the HBM roofline, by wall clock
+        "step_roofline_frac": round((ab["compress"] + ab["decompress"]) * K / wall / 1e9 / PEAK_GBPS, 4),
         "combined_roofline_frac": round((ab["compress"] + ab["decompress"]) /
                                         (t_c.mean() + t_d.mean()) / 1e9 / PEAK_GBPS, 4),
         "rel_rmse": {"fwht": round(rmse, 6), "no_fwht": round(rmse_nf, 6)},
     }
+    if not args.no_receiver:
+        result["receiver"] = receiver_timing(fp4q, inputs, torch, dev)
     if args.tradeoff:
         result["tradeoff"] = fwht_tradeoff(fp4q, inputs, torch, dev)
     if not args.no_cpu_baseline:

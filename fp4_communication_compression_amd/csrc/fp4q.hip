@@ -600,6 +600,33 @@ struct Peers {
     const float *block[FP4Q_MAX_PEERS];
 };
 
+// Sum of k payloads into R (mode kFma or kAdd) with kInFlight payloads' loads
+// outstanding: the loads of peer p + kInFlight are issued as soon as peer p has
+// been dequantised.  k is wave-uniform, so every branch here is uniform.
+#ifndef FP4Q_PEERS_IN_FLIGHT
+#define FP4Q_PEERS_IN_FLIGHT 4
+#endif
+constexpr int kInFlight = FP4Q_PEERS_IN_FLIGHT;
+
+template <DequantMode kMode>
+__device__ __forceinline__ void sum_peers(const Lane &L, const Peers &peers, int k, float (&R)[64]) {
+    PayloadRegs buf[kInFlight];
+#pragma unroll
+    for (int i = 0; i < kInFlight; ++i)
+        if (i < k) buf[i] = load_payload(L, peers.codes[i], peers.micro[i], peers.block[i]);
+    for (int p = 0; p < k; p += kInFlight) {
+#pragma unroll
+        for (int i = 0; i < kInFlight; ++i) {
+            if (p + i < k) {
+                dequant<kMode>(buf[i], R);
+                const int nx = p + i + kInFlight;
+                if (nx < k) buf[i] = load_payload(L, peers.codes[nx], peers.micro[nx], peers.block[nx]);
+            }
+        }
+    }
+}
+
+
 // Sum in the transform domain (the transform is linear), then one inverse
 // transform for all peers.
 template <bool kFwht, bool kBf16>
@@ -610,17 +637,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
     float R[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
-    // two payloads in flight: the next peer's loads are issued before the
-    // current peer is dequantised
-    PayloadRegs A = load_payload(L, peers.codes[0], peers.micro[0], peers.block[0]);
-    int p = 0;
-    for (; p + 2 <= k; p += 2) {
-        const PayloadRegs B = load_payload(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
-        dequant<kFma>(A, R);
-        if (p + 2 < k) A = load_payload(L, peers.codes[p + 2], peers.micro[p + 2], peers.block[p + 2]);
-        dequant<kFma>(B, R);
-    }
-    if (p < k) dequant<kFma>(A, R);
+    sum_peers<kFma>(L, peers, k, R);
     receiver_transform<kFwht, kBf16>(R);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
 }
@@ -643,15 +660,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     float R[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
-    PayloadRegs A = load_payload(L, peers.codes[0], peers.micro[0], peers.block[0]);
-    int p = 0;
-    for (; p + 2 <= k; p += 2) {
-        const PayloadRegs B = load_payload(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
-        dequant<kAdd>(A, R);
-        if (p + 2 < k) A = load_payload(L, peers.codes[p + 2], peers.micro[p + 2], peers.block[p + 2]);
-        dequant<kAdd>(B, R);
-    }
-    if (p < k) dequant<kAdd>(A, R);
+    sum_peers<kAdd>(L, peers, k, R);
 
     float s, t[4];
     unsigned mw, C[8];
