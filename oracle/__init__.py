@@ -217,3 +217,33 @@ def requantize(payloads, debug: bool = False):
         out["v"] = v
         out["t"] = t
     return out
+
+
+def compress_mx(x_bf16: np.ndarray, fwht: bool = True, debug: bool = False):
+    """MXFP4-style payload: dict(codes [rows, L/2] u8, scales [rows, L/32] u8 (E8M0)[, v])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    _check_shape(x)
+    rows, L = x.shape
+    codes = np.empty((rows, L // 2), np.uint8)
+    scales = np.empty((rows, L // 32), np.uint8)
+    v = np.empty((rows, L), np.float32) if debug else None
+    f = lib().fp4q_ref_compress_mx
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    f(_ptr(x), rows * L // BLOCK, int(bool(fwht)), _ptr(codes), _ptr(scales), _ptr(v) if debug else None)
+    out = {"codes": codes, "scales": scales}
+    if debug:
+        out["v"] = v
+    return out
+
+
+def decompress_mx(codes, scales, fwht: bool = True) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, half = codes.shape
+    L = 2 * half
+    out = np.empty((rows, L), np.float32)
+    f = lib().fp4q_ref_decompress_mx
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    f(_ptr(codes), _ptr(scales), rows * L // BLOCK, int(bool(fwht)), _ptr(out))
+    return out

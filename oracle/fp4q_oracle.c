@@ -304,6 +304,74 @@ void fp4q_ref_requantize(int k, const uint8_t *const *codes, const uint8_t *cons
     }
 }
 
+/* ------------------------------------------------ MXFP4-style variant
+ * The microscaling FP4 format named on the gist.science page ("Practical FP4
+ * Training for Large-Scale MoE Models on Hopper GPUs", Problemstellung item 2:
+ * blocks of 32, E2M1 elements), as an alternative to the dual scale: after the
+ * same transform, every 32 consecutive values share one power-of-two scale 2^e
+ * stored as an E8M0 byte (e + 127), with no coarse scale.  Following the OCP
+ * microscaling rule, e = floor(log2(max |y| over the 32)) - 2 (2 = the largest
+ * E2M1 exponent), clamped to [-127, 127]; a zero group takes e = -127.  Each
+ * element is v = y / 2^e (exact: a power-of-two scaling of a value below 8)
+ * rounded to E2M1 as in compress.  4.25 bits per element. */
+#define MXGROUP 32
+#define MXNGROUP (BLOCK / MXGROUP)
+
+static int mx_exponent(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    int e2;
+    (void)frexpf(amax, &e2); /* amax = f 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+    int e = (e2 - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+static void compress_block_mx(const uint16_t *x, int fwht, uint8_t *codes, uint8_t *scales,
+                              float *v_out) {
+    float y[BLOCK];
+    uint8_t code[BLOCK];
+    for (int i = 0; i < BLOCK; ++i) y[i] = widen_bf16(x[i]);
+    if (fwht) fp4q_ref_fwht256(y);
+    for (int g = 0; g < MXNGROUP; ++g) {
+        const float *yg = y + MXGROUP * g;
+        float a = 0.0f;
+        for (int i = 0; i < MXGROUP; ++i) a = fmaxf(a, fabsf(yg[i]));
+        int e = mx_exponent(a);
+        scales[g] = (uint8_t)(e + 127);
+        for (int i = 0; i < MXGROUP; ++i) {
+            float v = (float)ldexp((double)yg[i], -e); /* exact */
+            code[MXGROUP * g + i] = (uint8_t)fp4q_ref_e2m1_encode(v);
+            if (v_out) v_out[MXGROUP * g + i] = v;
+        }
+    }
+    for (int k = 0; k < BLOCK / 2; ++k)
+        codes[k] = (uint8_t)(code[2 * k] | (code[2 * k + 1] << 4));
+}
+
+void fp4q_ref_compress_mx(const uint16_t *x, int64_t nblocks, int fwht, uint8_t *codes,
+                          uint8_t *scales, float *v_out) {
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t b = 0; b < nblocks; ++b)
+        compress_block_mx(x + BLOCK * b, fwht, codes + (BLOCK / 2) * b, scales + MXNGROUP * b,
+                          v_out ? v_out + BLOCK * b : NULL);
+}
+
+/* yhat_i = E2M1value(code_i) * 2^e (exact), then the same transform. */
+void fp4q_ref_decompress_mx(const uint8_t *codes, const uint8_t *scales, int64_t nblocks,
+                            int fwht, float *out) {
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t b = 0; b < nblocks; ++b) {
+        float *o = out + BLOCK * b;
+        for (int e = 0; e < BLOCK; ++e) {
+            int c = (codes[(BLOCK / 2) * b + (e >> 1)] >> (4 * (e & 1))) & 15;
+            int ex = (int)scales[MXNGROUP * b + e / MXGROUP] - 127;
+            o[e] = (float)ldexp((double)fp4q_ref_e2m1_decode(c), ex);
+        }
+        if (fwht) fp4q_ref_fwht256(o);
+    }
+}
+
 /* ------------------------------------------------- vectorised scalar helpers */
 void fp4q_ref_e2m1_encode_n(const float *v, int64_t n, uint8_t *out) {
 #pragma omp parallel for schedule(static) num_threads(g_threads)
