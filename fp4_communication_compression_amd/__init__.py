@@ -59,11 +59,14 @@ def lib() -> ctypes.CDLL:
         L.fp4q_decompress_accumulate.argtypes = [I, PP, PP, PP, I64, I64, P, I, P]
         L.fp4q_decompress_accumulate_ex.argtypes = [I, PP, PP, PP, I64, I64, P, I, U32, P]
         L.fp4q_reduce_requantize.argtypes = [I, PP, PP, PP, I64, I64, P, P, P, P]
+        L.fp4q_compress_mx.argtypes = [P, I64, I64, P, P, U32, P]
+        L.fp4q_decompress_mx.argtypes = [P, P, I64, I64, P, I, U32, P]
         L.fp4q_status_str.argtypes = [I]
         L.fp4q_status_str.restype = ctypes.c_char_p
         for f in ("fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex", "fp4q_decompress",
                   "fp4q_decompress_ex", "fp4q_decompress_accumulate",
-                  "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize"):
+                  "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize",
+                  "fp4q_compress_mx", "fp4q_decompress_mx"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -188,3 +191,29 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
     _check(lib().fp4q_reduce_requantize(k, cast(cs), cast(ms), cast(bs), rows, L, _ptr(codes),
                                         _ptr(micro_scales), _ptr(block_scales), _stream(stream)))
     return codes, micro_scales, block_scales
+
+
+def fp4q_compress_mx(x, codes=None, scales=None, flags: int = 0, stream=None):
+    """MXFP4-style: bf16 [rows, L] -> (codes u8 [rows, L/2], E8M0 scales u8 [rows, L/32])."""
+    import torch
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("fp4q_compress_mx: input must hold bf16 bit patterns")
+    rows, L = _dims(x)
+    if codes is None:
+        codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, L // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_compress_mx(_ptr(x), rows, L, _ptr(codes), _ptr(scales), flags,
+                                  _stream(stream)))
+    return codes, scales
+
+
+def fp4q_decompress_mx(codes, scales, out=None, out_dtype=None, flags: int = 0, stream=None):
+    import torch
+    rows, half = _dims(codes)
+    L = 2 * half
+    if out is None:
+        out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
+    _check(lib().fp4q_decompress_mx(_ptr(codes), _ptr(scales), rows, L, _ptr(out),
+                                    _out_dtype_code(out.dtype), flags, _stream(stream)))
+    return out

@@ -673,6 +673,144 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     }
 }
 
+// --------------------------------------------------- MXFP4-style variant
+// Every 32 consecutive transformed values share one power-of-two scale 2^e,
+// e = floor(log2 max|y|) - 2 clamped to [-127, 127] (-127 for a zero group),
+// stored as an E8M0 byte e + 127; elements are E2M1(y / 2^e).  The conversion
+// instruction divides by the power of two of its scale operand, so the scale
+// costs no multiply.  After compress_transform a 32-group (index bits 0-4) is
+// register group k (bits 0-3) of the two quarters q, q ^ 1 (lane bit 4 = bit 4);
+// its number within the block is (q >> 1) + 2 k.
+__device__ __forceinline__ float pair_lane_max(float v) {  // max over lane bit 4
+    float a = v, b = v;
+    swap16(a, b);
+    return fmaxf(a, b);
+}
+
+template <bool kFwht>
+__global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
+    const uint4 *__restrict__ in, int64_t nblocks, uint4 *__restrict__ codes,
+    uint8_t *__restrict__ scales) {
+    __shared__ uint4 lds_all[kSenderWaves * kStageChunks];
+    const Lane L = lane_map<kSenderWaves>(nblocks);
+    uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
+    const int lane = L.lane, p = L.p, q = L.q;
+    {
+        uint4 d[8];
+        load_tile(in, L.tile, nblocks, lane, d);
+        uint4 *dst = lds + 33 * (lane >> 5) + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[66 * j] = d[j];
+    }
+    wave_lds_sync();
+    float R[64];
+    {
+        const uint4 *srcl = lds + 33 * p + 8 * q;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 x = srcl[i];
+            const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                R[8 * i + 2 * k] = as_f(w[k] << 16);
+                R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+            }
+        }
+    }
+    compress_transform<kFwht>(R);
+
+    // exponent of each 32-group; the registers hold 16 y when transformed
+    int e[4];
+    float scale[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(R[16 * k + i]));
+        m = pair_lane_max(m);
+        // floor(log2 m) = exponent field - 127 for normal m; zero or subnormal m
+        // clamps to -127 below.  16 y is exact, so floor(log2 max|y|) is 4 less.
+        int ek = (int)(as_u(m) >> 23) - 127 - (kFwht ? 4 : 0) - 2;
+        ek = ek < -127 ? -127 : (ek > 127 ? 127 : ek);
+        e[k] = ek;
+        // divisor applied by the conversion: 2^e (times 16 for 16 y), a normal
+        // float except for e = -127 without the transform: then the group's
+        // values (all below 2^-124) are doubled exactly and 2^-126 is used
+        int sh = ek + (kFwht ? 4 : 0);
+        if (!kFwht && sh == -127) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) R[16 * k + i] *= 2.0f;
+            sh = -126;
+        }
+        scale[k] = as_f((unsigned)(sh + 127) << 23);
+    }
+
+    unsigned C[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const float sc = scale[w >> 1];
+        unsigned c = 0;
+        static_for<4>([&](auto sel) {
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j], R[j + 1], sc, decltype(sel)::value);
+        });
+        C[w] = c;
+    }
+    // same re-dealing of code dwords as compress
+    swap32(C[0], C[2]);
+    swap32(C[1], C[3]);
+    swap32(C[4], C[6]);
+    swap32(C[5], C[7]);
+    swap16(C[0], C[2]);
+    swap16(C[1], C[3]);
+    swap16(C[4], C[6]);
+    swap16(C[5], C[7]);
+    wave_lds_sync();  // every lane has read its input chunks
+    store_codes(L, nblocks, lds, codes, C);
+    if (L.valid && (q & 1) == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) scales[L.b * 8 + (q >> 1) + 2 * k] = (uint8_t)(e[k] + 127);
+    }
+}
+
+// Receiver: register j of quarter q holds element 32 q + 128 (j >> 5) + (j & 31),
+// whose 32-group is q + 4 (j >> 5).
+template <bool kFwht, bool kBf16>
+__global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
+    const uint4 *__restrict__ codes, const uint2 *__restrict__ scales, int64_t nblocks,
+    void *__restrict__ out) {
+    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
+    const Lane L = lane_map<kReceiverWaves>(nblocks);
+    const uint4 *src = codes + L.bl * 8 + L.q;
+    const uint4 c0 = load_nt(src), c1 = load_nt(src + 4);
+    const uint2 sw = scales[L.bl];  // the block's 8 scale bytes
+    const int e0 = (int)((sw.x >> (8 * L.q)) & 0xFFu) - 127;  // group q
+    const int e1 = (int)((sw.y >> (8 * L.q)) & 0xFFu) - 127;  // group q + 4
+    const unsigned C[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float R[64];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = h ? e1 : e0;
+        // 2^e as the conversion's scale; 2^-127 is subnormal, so use 2^-126 and halve
+        const float sc = as_f((unsigned)((e < -126 ? -126 : e) + 127) << 23);
+#pragma unroll
+        for (int w = 4 * h; w < 4 * h + 4; ++w) {
+            static_for<4>([&](auto sel) {
+                const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], sc, decltype(sel)::value);
+                const int j = 8 * w + 2 * decltype(sel)::value;
+                R[j] = f[0];
+                R[j + 1] = f[1];
+            });
+        }
+        if (e < -126) {
+#pragma unroll
+            for (int j = 32 * h; j < 32 * h + 32; ++j) R[j] *= 0.5f;  // exact
+        }
+    }
+    receiver_transform<kFwht, kBf16>(R);
+    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
+}
+
 // ------------------------------------------------------------------- host
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -849,6 +987,44 @@ int fp4q_reduce_requantize(int k, const uint8_t *const *codes, const uint8_t *co
     }
     void *args[] = {&peers, &k, &nb, &out_codes, &out_micro, &out_block};
     return launch((const void *)&requantize_kernel, nb, kReceiverWaves, args, stream);
+}
+
+int fp4q_compress_mx(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
+                     uint8_t *scales, uint32_t flags, void *stream) {
+    int64_t n, nb;
+    int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (flags & ~(uint32_t)FP4Q_FLAG_NO_FWHT) return FP4Q_ERR_ARG;
+    if (n == 0) return FP4Q_OK;
+    if (!in_bf16 || !codes || !scales) return FP4Q_ERR_NULL;
+    if (!aligned(in_bf16, 16) || !aligned(codes, 16) || !aligned(scales, 8)) return FP4Q_ERR_ALIGN;
+    const Range in = rng(in_bf16, 2 * n), c = rng(codes, n / 2), sc = rng(scales, n / 32);
+    if (overlap(in, c) || overlap(in, sc) || overlap(c, sc)) return FP4Q_ERR_ARG;
+    void *args[] = {&in_bf16, &nb, &codes, &scales};
+    const void *fn = (flags & FP4Q_FLAG_NO_FWHT) ? (const void *)&compress_mx_kernel<false>
+                                                 : (const void *)&compress_mx_kernel<true>;
+    return launch(fn, nb, kSenderWaves, args, stream);
+}
+
+int fp4q_decompress_mx(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t row_len,
+                       void *out, int out_dtype, uint32_t flags, void *stream) {
+    int64_t n, nb;
+    int st = check_shape(rows, row_len, &n, &nb);
+    if (st != FP4Q_OK) return st;
+    if (flags & ~(uint32_t)FP4Q_FLAG_NO_FWHT) return FP4Q_ERR_ARG;
+    if (out_dtype != FP4Q_OUT_F32 && out_dtype != FP4Q_OUT_BF16) return FP4Q_ERR_ARG;
+    if (n == 0) return FP4Q_OK;
+    if (!codes || !scales || !out) return FP4Q_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 8) || !aligned(out, 16)) return FP4Q_ERR_ALIGN;
+    const Range o = rng(out, (out_dtype == FP4Q_OUT_F32 ? 4 : 2) * n);
+    if (overlap(o, rng(codes, n / 2)) || overlap(o, rng(scales, n / 32))) return FP4Q_ERR_ARG;
+    void *args[] = {&codes, &scales, &nb, &out};
+    const bool fw = !(flags & FP4Q_FLAG_NO_FWHT), bf = out_dtype == FP4Q_OUT_BF16;
+    const void *fn = fw ? (bf ? (const void *)&decompress_mx_kernel<true, true>
+                              : (const void *)&decompress_mx_kernel<true, false>)
+                        : (bf ? (const void *)&decompress_mx_kernel<false, true>
+                              : (const void *)&decompress_mx_kernel<false, false>);
+    return launch(fn, nb, kReceiverWaves, args, stream);
 }
 
 const char *fp4q_status_str(int status) {

@@ -139,6 +139,24 @@ int fp4q_reduce_requantize(int k, const uint8_t *const *codes,
                            uint8_t *out_codes, uint8_t *out_micro, float *out_block,
                            void *stream);
 
+/* MXFP4-style variant: the microscaling FP4 format (blocks of 32, E2M1
+ * elements) named on the gist.science page ("Practical FP4 Training for
+ * Large-Scale MoE Models on Hopper GPUs", Problemstellung item 2), applied
+ * after the same transform in place of the dual scale: every 32 consecutive
+ * transformed values y share one power-of-two scale 2^e with
+ * e = floor(log2 max|y|) - 2 clamped to [-127, 127] (-127 for a zero group),
+ * stored as the E8M0 byte e + 127; element codes are E2M1(y / 2^e) (round to
+ * nearest even, saturating, sign kept).  4.25 bits per element.
+ *   codes  N/2 bytes (as in fp4q_compress); scales N/32 bytes, 8-byte aligned
+ *   flags  0 or FP4Q_FLAG_NO_FWHT */
+int fp4q_compress_mx(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,
+                     uint8_t *scales, uint32_t flags, void *stream);
+
+/* Decode of the MXFP4-style payload: yhat = E2M1(code) * 2^e, then the same
+ * transform as fp4q_decompress; output fp32 or bf16 (out_dtype). */
+int fp4q_decompress_mx(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t row_len,
+                       void *out, int out_dtype, uint32_t flags, void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *fp4q_status_str(int status);
 

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex",
                             "fp4q_decompress", "fp4q_decompress_ex", "fp4q_decompress_accumulate",
                             "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize",
-                            "fp4q_status_str"])
+                            "fp4q_compress_mx", "fp4q_decompress_mx", "fp4q_status_str"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -138,3 +138,19 @@ def test_requantize_validation_order():
     assert req(1, cs, ms, bs, 1, 256, outs[0], outs[1] + 2, outs[2]) == fp4q.FP4Q_ERR_ALIGN
     assert req(1, cs, ms, bs, 4, 256, A + 16, outs[1], outs[2]) == fp4q.FP4Q_ERR_ARG   # over input codes
     assert req(1, cs, ms, bs, 4, 256, outs[0], outs[0] + 16, outs[2]) == fp4q.FP4Q_ERR_ARG
+
+
+def test_mx_validation_order():
+    big = 1 << 30
+    c = fp4q.lib().fp4q_compress_mx
+    d = fp4q.lib().fp4q_decompress_mx
+    assert c(A, 1, 300, A + big, A + 2 * big, 0, None) == fp4q.FP4Q_ERR_SHAPE
+    assert c(A, 1, 256, A + big, A + 2 * big, 2, None) == fp4q.FP4Q_ERR_ARG
+    assert c(NULL, 0, 256, NULL, NULL, 0, None) == fp4q.FP4Q_OK
+    assert c(A, 1, 256, A + big, NULL, 0, None) == fp4q.FP4Q_ERR_NULL
+    assert c(A, 1, 256, A + big, A + 2 * big + 4, 0, None) == fp4q.FP4Q_ERR_ALIGN
+    assert c(A, 4, 256, A + 64, A + 2 * big, 0, None) == fp4q.FP4Q_ERR_ARG
+    assert d(A, A + big, 1, 256, A + 2 * big, 3, 0, None) == fp4q.FP4Q_ERR_ARG
+    assert d(A, A + big, 1, 256, NULL, 0, 0, None) == fp4q.FP4Q_ERR_NULL
+    assert d(A, A + big + 4, 1, 256, A + 2 * big, 0, 0, None) == fp4q.FP4Q_ERR_ALIGN
+    assert d(A, A + big, 4, 256, A + 16, 0, 0, None) == fp4q.FP4Q_ERR_ARG

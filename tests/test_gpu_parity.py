@@ -203,3 +203,38 @@ def test_requantize_full_size(fp4q):
     torch.cuda.synchronize()
     st = parity.check_compress([o.cpu().numpy() for o in out], ref)
     _say("  %s" % st)
+
+
+def run_mx(fp4q, xb, fwht, name):
+    _say("mx case %s shape %s fwht %s" % (name, xb.shape, fwht))
+    flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+    ref = oracle.compress_mx(xb, fwht=fwht, debug=True)
+    c, sc = fp4q.fp4q_compress_mx(to_dev(xb), flags=flags)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sc.cpu().numpy(), ref["scales"])
+    gc, rc = parity.unpack(c.cpu().numpy()), parity.unpack(ref["codes"])
+    from tests import bruteforce as bfm
+    near = bfm.near(ref["v"].reshape(-1), bfm.e2m1_boundaries(), 1e-6)
+    assert np.all((gc == rc) | near)
+    assert np.count_nonzero(gc != rc) == 0
+    out = fp4q.fp4q_decompress_mx(to_dev(ref["codes"]), to_dev(ref["scales"]), flags=flags)
+    outb = fp4q.fp4q_decompress_mx(to_dev(ref["codes"]), to_dev(ref["scales"]),
+                                   out_dtype=torch.bfloat16, flags=flags)
+    torch.cuda.synchronize()
+    want = oracle.decompress_mx(ref["codes"], ref["scales"], fwht=fwht)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(outb.cpu().view(torch.int16).numpy().view(np.uint16),
+                                  inputs.f32_to_bf16_bits(want))
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+@pytest.mark.parametrize("name,make", SMALL[:4] + [("edge-mixed", lambda: inputs.make_edge_case("mixed_blocks", 24, 1024, seed=9)),
+                                               ("edge-tiny", lambda: inputs.make_edge_case("tiny", 24, 1024, seed=9)),
+                                               ("edge-zeros", lambda: inputs.make_edge_case("zeros", 8, 1024))],
+                         ids=[n for n, _ in SMALL[:4]] + ["edge-mixed", "edge-tiny", "edge-zeros"])
+def test_mx_parity(fp4q, name, make, fwht):
+    run_mx(fp4q, make(), fwht, name)
+
+
+def test_mx_full_size(fp4q):
+    run_mx(fp4q, inputs.make_config("large32768"), True, "large32768")
