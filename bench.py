@@ -86,6 +86,10 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> str:
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
                     vals.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        # the reference is the set of full-size copies: the largest copy dispatches
+        copies = sorted(vals.get("copy", []))
+        if copies:
+            vals["copy"] = [c for c in copies if c >= 0.9 * copies[-1]]
         return {k: float(np.median(v)) for k, v in vals.items()}
     fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     f_scale = COPY_REF_BYTES / (fetch["copy"] * 1024.0)
@@ -171,17 +175,28 @@ def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
         xb = inputs.make_config(name)
         x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         xf = x.double()
-        for flags, label in ((0, "fwht"), (fp4q.FP4Q_FLAG_NO_FWHT, "no_fwht")):
-            P = fp4q.fp4q_compress(x, flags=flags)
-            Y = fp4q.fp4q_decompress(*P, flags=flags)
+        for fmt, flags, label in (("dual", 0, "fwht"), ("dual", fp4q.FP4Q_FLAG_NO_FWHT, "no_fwht"),
+                                  ("mx", 0, "mx_fwht"), ("mx", fp4q.FP4Q_FLAG_NO_FWHT, "mx_no_fwht")):
+            if fmt == "dual":
+                P = fp4q.fp4q_compress(x, flags=flags)
+                Y = fp4q.fp4q_decompress(*P, flags=flags)
+
+                def once(P=P, Y=Y, flags=flags):
+                    fp4q.fp4q_compress(x, *P, flags=flags)
+                    fp4q.fp4q_decompress(*P, out=Y, flags=flags)
+            else:
+                P = fp4q.fp4q_compress_mx(x, flags=flags)
+                Y = fp4q.fp4q_decompress_mx(*P, flags=flags)
+
+                def once(P=P, Y=Y, flags=flags):
+                    fp4q.fp4q_compress_mx(x, *P, flags=flags)
+                    fp4q.fp4q_decompress_mx(*P, out=Y, flags=flags)
             for _ in range(5):
-                fp4q.fp4q_compress(x, *P, flags=flags)
-                fp4q.fp4q_decompress(*P, out=Y, flags=flags)
+                once()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(iters):
-                fp4q.fp4q_compress(x, *P, flags=flags)
-                fp4q.fp4q_decompress(*P, out=Y, flags=flags)
+                once()
             torch.cuda.synchronize()
             dt = (time.perf_counter() - t0) / iters
             rmse = float(torch.linalg.vector_norm(Y.double() - xf) / torch.linalg.vector_norm(xf))
