@@ -238,3 +238,59 @@ def test_mx_parity(fp4q, name, make, fwht):
 
 def test_mx_full_size(fp4q):
     run_mx(fp4q, inputs.make_config("large32768"), True, "large32768")
+
+
+def test_graph_capture_replay(fp4q):
+    """The entry points allocate nothing and never synchronise, so a compress +
+    decompress + reduce sequence can be captured in a HIP graph; every replay
+    (with eager work in between) must equal the eager result."""
+    xb = inputs.make_config("act2048", rows=256)
+    x = to_dev(xb)
+    codes, micro, block = fp4q.fp4q_compress(x)
+    out = fp4q.fp4q_decompress(codes, micro, block)
+    peers = [fp4q.fp4q_compress(to_dev(inputs.make_normal(256, 4096, seed=500 + p))) for p in range(3)]
+    acc = fp4q.fp4q_decompress_accumulate(peers)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (codes, micro, block, out, acc)]
+    for t in (codes, micro, block, out, acc):
+        t.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fp4q.fp4q_compress(x, codes, micro, block)
+            fp4q.fp4q_decompress(codes, micro, block, out=out)
+            fp4q.fp4q_decompress_accumulate(peers, out=acc)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        for t in (codes, micro, block, out, acc):
+            t.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((codes, micro, block, out, acc), want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d differs" % rep
+
+
+def test_concurrent_streams(fp4q):
+    """The library keeps no state: launches on two streams at once give the same
+    results as one at a time."""
+    xs = [to_dev(inputs.make_normal(512, 4096, seed=600 + i)) for i in range(2)]
+    ref = [[t.clone() for t in fp4q.fp4q_compress(x)] for x in xs]
+    ref_out = [fp4q.fp4q_decompress(*r) for r in ref]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    res = [None, None]
+    for _ in range(3):
+        for i, s in enumerate(streams):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                p = fp4q.fp4q_compress(xs[i])
+                res[i] = (p, fp4q.fp4q_decompress(*p))
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a, b in zip(res[i][0], ref[i]):
+                assert torch.equal(a, b)
+            assert torch.equal(res[i][1], ref_out[i])
