@@ -294,3 +294,61 @@ def test_concurrent_streams(fp4q):
             for a, b in zip(res[i][0], ref[i]):
                 assert torch.equal(a, b)
             assert torch.equal(res[i][1], ref_out[i])
+
+
+def test_offsets_beyond_32_bits(fp4q):
+    """N = 2^32 + 2^20 elements (rows of 4096): input, code, micro-scale and output
+    offsets all pass 2^31 and 2^32 bytes in the tail.  The tensor is a seeded
+    1024-row source gathered in a scrambled row order, so a block written to the
+    wrong place changes a sampled row.  Sampled rows on both sides of every
+    boundary are checked against the oracle; accumulate([P, P]) must equal
+    2 x decompress(P) bit for bit over the whole tensor (the sum of two equal
+    exact products is exact)."""
+    L, src_rows = 4096, 1024
+    rows = (1 << 20) + 256
+    n = rows * L
+    free, _ = torch.cuda.mem_get_info()
+    if free < 64 << 30:
+        pytest.skip("needs about 50 GiB of free device memory")
+    _say("offsets beyond 32 bits: %d x %d" % (rows, L))
+    xs = inputs.make_normal(src_rows, L, seed=900)
+    src_of = (np.arange(rows, dtype=np.int64) * 613 + 11) % src_rows
+    x = to_dev(xs).index_select(0, torch.from_numpy(src_of).to(DEV))
+    c, m, b = fp4q.fp4q_compress(x)
+    mc, ms = fp4q.fp4q_compress_mx(x)
+    del x
+    out = fp4q.fp4q_decompress(c, m, b)
+    torch.cuda.synchronize()
+
+    # rows holding element 2^29, 2^30, 2^31, 2^32 (fp32 output at 2^31 and 2^32
+    # bytes, bf16 input at 2^32 bytes, codes at 2^31 bytes) and their neighbours
+    edge = [e // L for e in (1 << 29, 1 << 30, 1 << 31, 1 << 32)]
+    rng = np.random.default_rng(901)
+    pick = sorted(set([0, 1, rows - 2, rows - 1] + [r + d for r in edge for d in (-1, 0)] +
+                      list(rng.integers(0, rows, 48))))
+    pick_d = torch.tensor(pick, device=DEV)
+    src = src_of[pick]
+    ref = oracle.compress(xs, debug=True)
+    ref_rows = {key: ref[key][src] for key in ref}
+    got = [t.index_select(0, pick_d).cpu().numpy() for t in (c, m, b)]
+    st = parity.check_compress(got, ref_rows)
+    assert st["code_mismatch"] == 0 and st["micro_mismatch"] == 0
+    want = oracle.decompress(*got)
+    o = out.index_select(0, pick_d).cpu().numpy()
+    np.testing.assert_array_equal(o.view(np.uint32), want.view(np.uint32))
+
+    refmx = oracle.compress_mx(xs)
+    np.testing.assert_array_equal(ms.index_select(0, pick_d).cpu().numpy(), refmx["scales"][src])
+    np.testing.assert_array_equal(mc.index_select(0, pick_d).cpu().numpy(), refmx["codes"][src])
+    del mc, ms
+
+    acc = fp4q.fp4q_decompress_accumulate([(c, m, b), (c, m, b)])
+    acc_bf = fp4q.fp4q_decompress_accumulate([(c, m, b), (c, m, b)], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    out.mul_(2.0)
+    assert torch.equal(acc, out)
+    ob = acc_bf.index_select(0, pick_d).cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ob, inputs.f32_to_bf16_bits(2.0 * want))
+    assert n > (1 << 32)
+    del acc, acc_bf, out, c, m, b
+    torch.cuda.empty_cache()
