@@ -449,16 +449,19 @@ struct PayloadRegs {
     float s;
 };
 
+// The block's 16 micro-scale bytes arrive in one 16-byte load (the four lanes of
+// a block read the same 16 bytes); each lane keeps its two byte pairs.
 __device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *__restrict__ codes,
-                                                    const unsigned *__restrict__ micro,
+                                                    const uint4 *__restrict__ micro,
                                                     const float *__restrict__ block) {
     PayloadRegs P;
     const uint4 *src = codes + L.bl * 8 + L.q;
     P.c0 = load_nt(src);
     P.c1 = load_nt(src + 4);
+    const uint4 m = micro[L.bl];
     const unsigned sh = 16u * (L.q & 1);
-    P.lo = micro[L.bl * 4 + (L.q >> 1)] >> sh;
-    P.hi = micro[L.bl * 4 + 2 + (L.q >> 1)] >> sh;
+    P.lo = ((L.q >> 1) ? m.y : m.x) >> sh;
+    P.hi = ((L.q >> 1) ? m.w : m.z) >> sh;
     P.s = block[L.bl];
     return P;
 }
@@ -583,7 +586,7 @@ __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 
 
 template <bool kFwht, bool kBf16>
 __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
-    const uint4 *__restrict__ codes, const unsigned *__restrict__ micro,
+    const uint4 *__restrict__ codes, const uint4 *__restrict__ micro,
     const float *__restrict__ block, int64_t nblocks, void *__restrict__ out) {
     __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
 // --------------------------------------------------- receiver-side reduce
 struct Peers {
     const uint4 *codes[FP4Q_MAX_PEERS];
-    const unsigned *micro[FP4Q_MAX_PEERS];
+    const uint4 *micro[FP4Q_MAX_PEERS];
     const float *block[FP4Q_MAX_PEERS];
 };
 
@@ -841,7 +844,7 @@ int launch(const void *fn, int64_t nb, int waves, void **args, void *stream) {
 
 int check_payload_ptrs(const void *codes, const void *micro, const void *block) {
     if (!codes || !micro || !block) return FP4Q_ERR_NULL;
-    if (!aligned(codes, 16) || !aligned(micro, 4) || !aligned(block, 4)) return FP4Q_ERR_ALIGN;
+    if (!aligned(codes, 16) || !aligned(micro, 16) || !aligned(block, 4)) return FP4Q_ERR_ALIGN;
     return FP4Q_OK;
 }
 
@@ -940,7 +943,7 @@ int fp4q_decompress_accumulate_ex(int k, const uint8_t *const *codes,
             overlap(o, rng(block_scales[p], 4 * nb)))
             return FP4Q_ERR_ARG;
         peers.codes[p] = reinterpret_cast<const uint4 *>(codes[p]);
-        peers.micro[p] = reinterpret_cast<const unsigned *>(micro_scales[p]);
+        peers.micro[p] = reinterpret_cast<const uint4 *>(micro_scales[p]);
         peers.block[p] = block_scales[p];
     }
     void *args[] = {&peers, &k, &nb, &out};
@@ -982,7 +985,7 @@ int fp4q_reduce_requantize(int k, const uint8_t *const *codes, const uint8_t *co
         for (const Range o : {oc, om, ob})
             if (overlap(o, ic) || overlap(o, im) || overlap(o, ib)) return FP4Q_ERR_ARG;
         peers.codes[p] = reinterpret_cast<const uint4 *>(codes[p]);
-        peers.micro[p] = reinterpret_cast<const unsigned *>(micro_scales[p]);
+        peers.micro[p] = reinterpret_cast<const uint4 *>(micro_scales[p]);
         peers.block[p] = block_scales[p];
     }
     void *args[] = {&peers, &k, &nb, &out_codes, &out_micro, &out_block};

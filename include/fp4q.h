@@ -34,8 +34,10 @@
  *     (FP4Q_ERR_ARG), then pointers (FP4Q_ERR_NULL), alignment
  *     (FP4Q_ERR_ALIGN), overlap (FP4Q_ERR_ARG).  rows == 0 returns FP4Q_OK
  *     before the pointer checks and launches nothing.
- *   - Alignment: bf16 input, codes and outputs 16 bytes; micro_scales and
- *     block_scales 4 bytes.
+ *   - Alignment: bf16 input, codes, micro_scales and outputs 16 bytes;
+ *     block_scales 4 bytes.  (A payload packed into one buffer as codes, then
+ *     micro-scales, then block scales meets this when the buffer is 16-byte
+ *     aligned: the codes take N/2 bytes, a multiple of 128.)
  *   - A failed launch returns FP4Q_ERR_LAUNCH.
  *   - Inputs must be finite with |x| < 2^118; this is not checked.
  */

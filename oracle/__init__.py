@@ -29,7 +29,7 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (binary32 semantics: no contraction, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC])
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

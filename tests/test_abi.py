@@ -79,6 +79,7 @@ def test_compress_validation_order():
     assert comp(A + 2, 1, 256, A + big, A + 2 * big, A + 3 * big) == fp4q.FP4Q_ERR_ALIGN
     assert comp(A, 1, 256, A + big + 4, A + 2 * big, A + 3 * big) == fp4q.FP4Q_ERR_ALIGN
     assert comp(A, 1, 256, A + big, A + 2 * big + 2, A + 3 * big) == fp4q.FP4Q_ERR_ALIGN
+    assert comp(A, 1, 256, A + big, A + 2 * big + 4, A + 3 * big) == fp4q.FP4Q_ERR_ALIGN  # micro: 16
     assert comp(A, 1, 256, A + big, A + 2 * big, A + 3 * big + 1) == fp4q.FP4Q_ERR_ALIGN
     # overlaps: codes inside the input, micro on codes, block on micro
     assert comp(A, 4, 256, A + 16, A + 2 * big, A + 3 * big) == fp4q.FP4Q_ERR_ARG
@@ -97,6 +98,7 @@ def test_decompress_validation_order():
     assert decomp(NULL, A + big, A + 2 * big, 1, 256, A + 3 * big) == fp4q.FP4Q_ERR_NULL
     assert decomp(*args, 1, 256, A + 3 * big + 8) == fp4q.FP4Q_ERR_ALIGN
     assert decomp(A + 8, A + big, A + 2 * big, 1, 256, A + 3 * big) == fp4q.FP4Q_ERR_ALIGN
+    assert decomp(A, A + big + 4, A + 2 * big, 1, 256, A + 3 * big) == fp4q.FP4Q_ERR_ALIGN
     assert decomp(*args, 4, 256, A + 64) == fp4q.FP4Q_ERR_ARG        # output over the codes
 
 
@@ -114,6 +116,7 @@ def test_accumulate_validation_order():
     assert acc(2, cs + [NULL], ms * 2, bs * 2, 1, 256, out) == fp4q.FP4Q_ERR_NULL
     assert acc(1, cs, ms, bs, 1, 256, out + 4) == fp4q.FP4Q_ERR_ALIGN
     assert acc(2, cs + [A + 4], ms * 2, bs * 2, 1, 256, out) == fp4q.FP4Q_ERR_ALIGN
+    assert acc(2, cs * 2, ms + [A + big + 8], bs * 2, 1, 256, out) == fp4q.FP4Q_ERR_ALIGN
     assert acc(1, [out + 16], ms, bs, 4, 256, out) == fp4q.FP4Q_ERR_ARG   # overlap with out
 
 
@@ -136,6 +139,8 @@ def test_requantize_validation_order():
     assert req(2, cs + [NULL], ms * 2, bs * 2, 1, 256, *outs) == fp4q.FP4Q_ERR_NULL
     assert req(1, cs, ms, bs, 1, 256, outs[0] + 8, outs[1], outs[2]) == fp4q.FP4Q_ERR_ALIGN
     assert req(1, cs, ms, bs, 1, 256, outs[0], outs[1] + 2, outs[2]) == fp4q.FP4Q_ERR_ALIGN
+    assert req(1, cs, ms, bs, 1, 256, outs[0], outs[1] + 4, outs[2]) == fp4q.FP4Q_ERR_ALIGN
+    assert req(1, cs, [A + big + 4], bs, 1, 256, *outs) == fp4q.FP4Q_ERR_ALIGN
     assert req(1, cs, ms, bs, 4, 256, A + 16, outs[1], outs[2]) == fp4q.FP4Q_ERR_ARG   # over input codes
     assert req(1, cs, ms, bs, 4, 256, outs[0], outs[0] + 16, outs[2]) == fp4q.FP4Q_ERR_ARG
 
