@@ -37,6 +37,7 @@ METRIC = "compress+decompress GB/s of bf16 input and % HBM roofline, 32768x4096"
 PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "fp4_communication_compression_amd", "csrc", "fp4q.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_large32768.md")
+RECEIVER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_reduce_k8.md")
 COPY_REF_BYTES = 256 << 20
 EVENT_EVERY = 8
 
@@ -55,38 +56,64 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was taken on
-    the current kernel source (else None)."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def measured_traffic(path: str = None):
+    """HBM bytes per launch, per kernel, from a committed counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = path or TRAFFIC_SUMMARY
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_SUMMARY).read()
-    m = re.search(r"traffic: source=(\w+) compress=(\d+) decompress=(\d+)", text)
+    text = open(path).read()
+    m = re.search(r"traffic: source=(\w+)((?: \w+=\d+)*)", text)
     if not m or m.group(1) != kernel_source_hash():
         return None
-    return {"compress": int(m.group(2)), "decompress": int(m.group(3))}
+    return {k: int(v) for k, v in re.findall(r"(\w+)=(\d+)", m.group(2))}
 
 
 def _short(kernel_name: str) -> str:
-    if "decompress_kernel" in kernel_name:
-        return "decompress"
-    if "compress_kernel" in kernel_name:
-        return "compress"
+    for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate", "requantize"):
+        if fam + "_kernel" in kernel_name:
+            return fam
     if "copyBuffer" in kernel_name:
         return "copy"
     return kernel_name.split("(")[0][:40]
+
+
+REDUCE_N = 4096 * 11008          # elements per peer of the k = 8 reduce workload
+REDUCE_K = 8
+
+
+def _receiver_bytes():
+    n = REDUCE_N
+    pay = n // 2 + n // 16 + n // 64
+    return {"accumulate": REDUCE_K * pay + 4 * n, "requantize": (REDUCE_K + 1) * pay}
+
+
+def _largest_grid(rows, grid_key):
+    """Per kernel family, the dispatches of its largest grid (the workload the
+    bench times; smaller launches of the same kernel are set-up or other shapes)."""
+    by = {}
+    for r in rows:
+        by.setdefault(_short(r["Kernel_Name"]), []).append(r)
+    out = {}
+    for fam, rs in by.items():
+        g = max(int(r[grid_key]) for r in rs)
+        out[fam] = [r for r in rs if int(r[grid_key]) == g]
+    return out
 
 
 def summarize_counters(fetch_dir: str, write_dir: str) -> str:
     """Counter summary (markdown) from two rocprofv3 --pmc runs of this bench with
     --copy-reference: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by what
     the same counters read for a plain device copy of COPY_REF_BYTES."""
+    grids = {}
+
     def load(d, counter):
-        vals = {}
+        rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] == counter:
-                    vals.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        fams = _largest_grid(rows, "Grid_Size")
+        grids.update({k: int(v[0]["Grid_Size"]) for k, v in fams.items()})
+        vals = {k: [float(r["Counter_Value"]) for r in v] for k, v in fams.items()}
         # the reference is the set of full-size copies: the largest copy dispatches
         copies = sorted(vals.get("copy", []))
         if copies:
@@ -95,36 +122,51 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> str:
     fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     f_scale = COPY_REF_BYTES / (fetch["copy"] * 1024.0)
     w_scale = COPY_REF_BYTES / (write["copy"] * 1024.0)
-    n = 32768 * 4096
-    ab = algorithmic_bytes(n)
-    out = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) | algorithmic bytes | ratio |",
-           "|---|---|---|---|---|---|"]
+    ab = dict(algorithmic_bytes(32768 * 4096))
+    ab.update(_receiver_bytes())
+    out = ["| kernel | workload | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) | algorithmic bytes | ratio |",
+           "|---|---|---|---|---|---|---|"]
     traffic = {}
-    for k in ("compress", "decompress"):
+    for k in ("compress", "decompress", "accumulate", "requantize"):
+        # only launches of the workload each figure is defined for (one thread per 64 elements)
+        head = k in ("compress", "decompress")
+        want_grid = (32768 * 4096 if head else REDUCE_N) // 64
+        if k not in fetch or k not in write or grids[k] != want_grid:
+            continue
         t = fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale
         traffic[k] = int(round(t))
-        out.append("| %s | %.0f | %.0f | %d | %d | %.3f |" % (k, fetch[k], write[k], traffic[k], ab[k], t / ab[k]))
-    out.append("| copy (%d B) | %.0f | %.0f | scale factors: fetch x%.3f, write x%.3f | | |"
+        wl = "32768x4096" if head else "k=8 x 4096x11008"
+        out.append("| %s | %s | %.0f | %.0f | %d | %d | %.3f |" % (k, wl, fetch[k], write[k], traffic[k],
+                                                                 ab[k], t / ab[k]))
+    out.append("| copy (%d B) | | %.0f | %.0f | scale factors: fetch x%.3f, write x%.3f | | |"
                % (COPY_REF_BYTES, fetch["copy"], write["copy"], f_scale, w_scale))
     out.append("")
-    out.append("traffic: source=%s compress=%d decompress=%d" % (kernel_source_hash(), traffic["compress"],
-                                                                 traffic["decompress"]))
+    out.append("traffic: source=%s " % kernel_source_hash() +
+               " ".join("%s=%d" % (k, v) for k, v in traffic.items()))
     return "\n".join(out)
 
 
 def summarize_trace(trace_dir: str) -> str:
-    """Kernel durations from a rocprofv3 --kernel-trace --stats run (markdown)."""
+    """Per-dispatch kernel durations from a rocprofv3 --kernel-trace run (markdown):
+    each of this library's kernel instantiations at its largest grid."""
     rows = []
-    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         rows += list(csv.DictReader(open(f)))
-    out = ["| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    groups = {}
     for r in rows:
-        name = _short(r["Name"])
-        if name in ("compress", "decompress", "copy"):
-            m = re.search(r"((?:de)?compress_kernel<[^>]*>|__amd_rocclr_copyBuffer\w*)", r["Name"])
-            out.append("| %s | %s | %.2f | %.2f | %.2f |" % (
-                m.group(1) if m else name, r["Calls"], float(r["AverageNs"]) / 1e3,
-                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel)",
+                      r["Kernel_Name"])
+        if not m:
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups.setdefault(m.group(1), []).append((grid, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    out = ["| kernel | grid (threads) | calls | average us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
+    for name in sorted(groups, key=lambda n: -len(groups[n])):
+        g = max(x[0] for x in groups[name])
+        d = np.array([x[1] for x in groups[name] if x[0] == g])
+        out.append("| %s | %d | %d | %.2f | %.2f | %.2f | %.2f |" % (
+            name, g, len(d), d.mean(), float(np.median(d)), d.min(), d.max()))
     return "\n".join(out)
 
 
@@ -169,7 +211,8 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
                      "min_us": round(t.min() * 1e6, 2),
                      "p90_us": round(float(np.percentile(t, 90)) * 1e6, 2),
                      "algorithmic_bytes": nbytes, "achieved_GBps": round(gbps, 1),
-                     "frac": round(gbps / PEAK_GBPS, 4)}
+                     "frac": round(gbps / PEAK_GBPS, 4),
+                     "traffic": (measured_traffic(RECEIVER_TRAFFIC_SUMMARY) or {}).get(name.split("_")[-1])}
         log("receiver %-22s median %7.1f us (avg %.1f, p90 %.1f)  %7.1f GB/s  %.1f%% of HBM peak" % (
             name, med * 1e6, t.mean() * 1e6, res[name]["p90_us"], gbps, 100 * gbps / PEAK_GBPS))
     res["workload"] = "k=8 peers of bf16 4096x11008 N(0,1e-3), seeds 4..11"
@@ -268,6 +311,25 @@ def cpu_baseline(xb: np.ndarray, target_s: float = 3.0, runs: int = 3):
             "cpu_model": _cpu_model(), "legs": legs}
 
 
+def copy_reference(torch, dev):
+    """Three plain device-to-device copies of COPY_REF_BYTES (the runtime's blit
+    kernel): the scale reference for the HBM byte counters."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    src = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        rc = hip.hipMemcpyAsync(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                COPY_REF_BYTES, 3, stream)  # 3 = device to device
+        if rc != 0:
+            raise RuntimeError("hipMemcpyAsync failed: %d" % rc)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +339,9 @@ def main():
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-receiver", action="store_true",
                     help="skip the receiver-kernel timings on the k=8 reduce workload")
+    ap.add_argument("--receiver-only", action="store_true",
+                    help="time only the receiver kernels on the k=8 reduce workload (for profiling) "
+                         "and print their JSON")
     ap.add_argument("--tradeoff", action="store_true",
                     help="also report throughput and error with and without the transform "
                          "on the 2048x4096 and 8192x4096 workloads")
@@ -305,6 +370,11 @@ def main():
 
     fp4q.lib()
     dev = torch.device("cuda:0")
+    if args.receiver_only:
+        if args.copy_reference:
+            copy_reference(torch, dev)
+        print(json.dumps({"receiver": receiver_timing(fp4q, inputs, torch, dev)}), flush=True)
+        return
     rows, L = 32768, 4096
     n = rows * L
     log("generating large32768 (%dx%d) ..." % (rows, L))
@@ -328,21 +398,7 @@ def main():
             ev[2].record()
 
     if args.copy_reference:
-        # plain device-to-device copy of known size: the runtime's blit kernel
-        import ctypes
-        hip = ctypes.CDLL("libamdhip64.so")
-        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                       ctypes.c_int, ctypes.c_void_p]
-        src = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for _ in range(3):
-            rc = hip.hipMemcpyAsync(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
-                                    COPY_REF_BYTES, 3, stream)  # 3 = device to device
-            if rc != 0:
-                raise RuntimeError("hipMemcpyAsync failed: %d" % rc)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_reference(torch, dev)
 
     log("warmup %d" % args.warmup)
     for i in range(args.warmup):
