@@ -255,7 +255,7 @@ def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
             rmse = float(torch.linalg.vector_norm(Y.double() - xf) / torch.linalg.vector_norm(xf))
             rows_out.append({"workload": name, "transform": label, "us_per_step": round(dt * 1e6, 1),
                              "GBps_bf16_in": round(2 * x.numel() / dt / 1e9, 1),
-                             "rel_rmse": round(rmse, 6)})
+                             "rel_rmse": round(rmse, 6), "cache_resident": True})
             log("tradeoff %-12s %-8s %7.1f us  %7.1f GB/s  rel RMSE %.6f" % (
                 name, label, dt * 1e6, 2 * x.numel() / dt / 1e9, rmse))
     return rows_out
@@ -304,11 +304,24 @@ def cpu_baseline(xb: np.ndarray, target_s: float = 3.0, runs: int = 3):
                        "median_s": round(tt, 3)}
         log("cpu oracle %-13s %2d threads, %5d rows: %.4f GB/s (median of %d)" % (
             label, th, rows, legs[label]["GBps"], runs))
+    # the other workloads, whole: median of `runs`, all cores and one thread
+    from fp4_communication_compression_amd import inputs
+    per_config = {}
+    for name in ("act2048", "outlier8192"):
+        xc = inputs.make_config(name)
+        per_config[name] = {}
+        for label, th in (("all_cores", threads), ("single_thread", 1)):
+            oracle.set_threads(th)
+            tt = float(np.median([sum(once(xc)) for _ in range(runs)]))
+            per_config[name][label + "_GBps"] = round(2 * xc.size / tt / 1e9, 4)
+        log("cpu oracle %-12s all cores %.4f GB/s, one thread %.4f GB/s" % (
+            name, per_config[name]["all_cores_GBps"], per_config[name]["single_thread_GBps"]))
+    oracle.set_threads(threads)
     a = legs["all_cores"]
     return {"value": a["GBps"], "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
             "sample": "first %d of %d rows (x4096), compress then decompress, median of %d runs "
                       "(%.1f s each)" % (a["rows"], xb.shape[0], runs, a["median_s"]),
-            "cpu_model": _cpu_model(), "legs": legs}
+            "cpu_model": _cpu_model(), "legs": legs, "other_workloads": per_config}
 
 
 def copy_reference(torch, dev):
@@ -342,9 +355,9 @@ def main():
     ap.add_argument("--receiver-only", action="store_true",
                     help="time only the receiver kernels on the k=8 reduce workload (for profiling) "
                          "and print their JSON")
-    ap.add_argument("--tradeoff", action="store_true",
-                    help="also report throughput and error with and without the transform "
-                         "on the 2048x4096 and 8192x4096 workloads")
+    ap.add_argument("--no-tradeoff", action="store_true",
+                    help="skip the throughput and error report with and without the transform "
+                         "on the 2048x4096 and 8192x4096 workloads (cache-resident)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain %d-byte device copy (counter scale reference)" % COPY_REF_BYTES)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -471,7 +484,7 @@ def main():
     }
     if not args.no_receiver:
         result["receiver"] = receiver_timing(fp4q, inputs, torch, dev)
-    if args.tradeoff:
+    if not args.no_tradeoff:
         result["tradeoff"] = fwht_tradeoff(fp4q, inputs, torch, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
