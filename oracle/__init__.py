@@ -190,27 +190,41 @@ def rel_rmse(x_bf16: np.ndarray, xhat: np.ndarray) -> float:
     return float(np.sqrt(np.sum(d * d))) / nx if nx > 0 else 0.0
 
 
-def requantize(payloads, debug: bool = False):
-    """Sum of k payloads in the transform domain (fp32, peer order), quantised again:
-    returns dict(codes, micro, block[, v, t]) of the same shape as the inputs."""
+def requantize(payloads, debug: bool = False, local=None, fwht: bool = True):
+    """Sum of k payloads in the transform domain (fp32, peer order), quantised again;
+    with ``local`` (bf16 bit patterns of the same shape) the accumulator starts at
+    that slice transformed as compress transforms it (as is when ``fwht`` is off).
+    Returns dict(codes, micro, block[, v, t]) of the same shape as the inputs."""
     k = len(payloads)
+    if k:
+        rows, half = np.asarray(payloads[0][0]).shape
+        L = 2 * half
+    else:
+        if local is None:
+            raise ValueError("requantize needs a payload or a local slice")
+        rows, L = np.asarray(local).shape
+    if local is not None:
+        local = np.ascontiguousarray(local, dtype=np.uint16)
+        _check_shape(local)
+        if local.shape != (rows, L):
+            raise ValueError("local slice shape differs from the payloads'")
     cs = [np.ascontiguousarray(p[0], np.uint8) for p in payloads]
     ms = [np.ascontiguousarray(p[1], np.uint8) for p in payloads]
     bs = [np.ascontiguousarray(p[2], np.float32) for p in payloads]
-    rows, half = cs[0].shape
-    L = 2 * half
     nb = rows * L // BLOCK
     codes = np.empty((rows, L // 2), np.uint8)
     micro = np.empty((rows, L // GROUP), np.uint8)
     block = np.empty((rows, L // BLOCK), np.float32)
     v = np.empty((rows, L), np.float32) if debug else None
     t = np.empty((rows, L // GROUP), np.float32) if debug else None
-    PA = ctypes.c_void_p * k
-    f = lib().fp4q_ref_requantize
-    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    PA = ctypes.c_void_p * max(k, 1)
+    f = lib().fp4q_ref_requantize_ex
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
     f(k, PA(*[c.ctypes.data for c in cs]), PA(*[m.ctypes.data for m in ms]),
-      PA(*[b.ctypes.data for b in bs]), nb, _ptr(codes), _ptr(micro), _ptr(block),
+      PA(*[b.ctypes.data for b in bs]), _ptr(local) if local is not None else None,
+      int(bool(fwht)), nb, _ptr(codes), _ptr(micro), _ptr(block),
       _ptr(v) if debug else None, _ptr(t) if debug else None)
     out = {"codes": codes, "micro": micro, "block": block}
     if debug:

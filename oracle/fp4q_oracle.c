@@ -281,20 +281,30 @@ void fp4q_ref_accumulate_f64(int k, const uint8_t *const *codes, const uint8_t *
 }
 
 /* Receiver step of a compressed AllReduce split into a reduce-scatter and an
- * all-gather: the k payloads a rank receives for its slice are summed and the
- * sum is quantised again for the all-gather.  Reading: the sum is taken where
- * the payloads live, in the transform domain (decompressing k payloads, summing
- * and compressing again would apply H/16 twice, and H/16 is its own inverse), in
- * fp32, each term E2M1value(code) * S_g as in decompress, added in peer order
- * p = 0 .. k-1 to an accumulator that starts at +0; then the quantisation
- * steps of compress (block maximum onwards) apply to the sum. */
-void fp4q_ref_requantize(int k, const uint8_t *const *codes, const uint8_t *const *micro,
-                         const float *const *block, int64_t nblocks, uint8_t *out_codes,
-                         uint8_t *out_micro, float *out_block, float *v_out, float *t_out) {
+ * all-gather: the k payloads a rank receives for its slice are summed, together
+ * with the rank's own uncompressed part of that slice when one is given, and
+ * the sum is quantised again for the all-gather.  Reading: the sum is taken
+ * where the payloads live, in the transform domain (decompressing k payloads,
+ * summing and compressing again would apply H/16 twice, and H/16 is its own
+ * inverse), in fp32.  The accumulator starts at the local part transformed
+ * exactly as compress transforms its input (fwht = 0: the local part as is),
+ * or at +0 without one; each peer's term E2M1value(code) * S_g, as in
+ * decompress, is then added in peer order p = 0 .. k-1 (a rounded product and
+ * a rounded sum); then the quantisation steps of compress (block maximum
+ * onwards) apply to the sum.  With no peer the result is compress(local). */
+void fp4q_ref_requantize_ex(int k, const uint8_t *const *codes, const uint8_t *const *micro,
+                            const float *const *block, const uint16_t *local, int fwht,
+                            int64_t nblocks, uint8_t *out_codes, uint8_t *out_micro,
+                            float *out_block, float *v_out, float *t_out) {
 #pragma omp parallel for schedule(static) num_threads(g_threads)
     for (int64_t b = 0; b < nblocks; ++b) {
         float acc[BLOCK], d[BLOCK];
-        for (int i = 0; i < BLOCK; ++i) acc[i] = 0.0f;
+        if (local) {
+            for (int i = 0; i < BLOCK; ++i) acc[i] = widen_bf16(local[BLOCK * b + i]);
+            if (fwht) fp4q_ref_fwht256(acc);
+        } else {
+            for (int i = 0; i < BLOCK; ++i) acc[i] = 0.0f;
+        }
         for (int p = 0; p < k; ++p) {
             decompress_block(codes[p] + (BLOCK / 2) * b, micro[p] + NGROUP * b, block[p][b], 0, d);
             for (int i = 0; i < BLOCK; ++i) acc[i] = acc[i] + d[i];
@@ -302,6 +312,13 @@ void fp4q_ref_requantize(int k, const uint8_t *const *codes, const uint8_t *cons
         quantize_block(acc, out_codes + (BLOCK / 2) * b, out_micro + NGROUP * b, out_block + b,
                        v_out ? v_out + BLOCK * b : NULL, t_out ? t_out + NGROUP * b : NULL);
     }
+}
+
+void fp4q_ref_requantize(int k, const uint8_t *const *codes, const uint8_t *const *micro,
+                         const float *const *block, int64_t nblocks, uint8_t *out_codes,
+                         uint8_t *out_micro, float *out_block, float *v_out, float *t_out) {
+    fp4q_ref_requantize_ex(k, codes, micro, block, NULL, 1, nblocks, out_codes, out_micro,
+                           out_block, v_out, t_out);
 }
 
 /* ------------------------------------------------ MXFP4-style variant

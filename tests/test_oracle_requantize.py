@@ -35,11 +35,10 @@ def _transform_domain_sum(payloads):
     return acc
 
 
-@pytest.mark.parametrize("k", [1, 3, 8])
-def test_requantize_against_brute_force(k):
-    pay = _payloads(k)
-    got = oracle.requantize(pay, debug=True)
-    y = _transform_domain_sum(pay).astype(np.float64)
+def _check_quantised(got, y):
+    """Brute-force re-quantisation of the fp32 sum y [blocks, 256] (as float64):
+    block scales to 1e-6, micro-scales and codes by nearest-code search, exempt
+    within 1e-6 of a rounding boundary."""
     A = np.abs(y).max(axis=1)
     s = A / 2688.0
     np.testing.assert_allclose(got["block"].reshape(-1), s, rtol=1e-6)
@@ -56,6 +55,57 @@ def test_requantize_against_brute_force(k):
     near_c = bf.near(v.reshape(-1, 256), bf.e2m1_boundaries(), 1e-6) | np.repeat(near_m, 16, axis=1)
     gc = unpack(got["codes"]).reshape(-1, 256)
     assert np.all((gc == codes) | near_c)
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_requantize_against_brute_force(k):
+    pay = _payloads(k)
+    got = oracle.requantize(pay, debug=True)
+    _check_quantised(got, _transform_domain_sum(pay).astype(np.float64))
+
+
+def _local_slice(rows=6, L=1024, seed=60):
+    """bf16 local slice of small multiples of 2^-10 (|x| <= 8 * 2^-10): every sum
+    of the transform is exact in fp32, so the dense binary64 Hadamard product
+    equals the radix-2 result exactly."""
+    rng = np.random.default_rng(seed)
+    x = (rng.integers(-8, 9, (rows, L)) * 2.0 ** -10).astype(np.float32)
+    return inputs.f32_to_bf16_bits(x), x
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+@pytest.mark.parametrize("k", [0, 1, 3])
+def test_requantize_with_local_against_brute_force(k, fwht):
+    """The accumulator starts at the local slice, transformed (dense H/16) or as
+    is, then each peer's decoded payload is added in fp32, in peer order."""
+    xb, x = _local_slice()
+    pay = []
+    for p in range(k):
+        r = oracle.compress(inputs.make_normal(6, 1024, seed=70 + p, scale=1e-3), fwht=fwht)
+        pay.append((r["codes"], r["micro"], r["block"]))
+    got = oracle.requantize(pay, debug=True, local=xb, fwht=fwht)
+    blocks = x.astype(np.float64).reshape(-1, 256)
+    acc = ((blocks @ bf.H256.T) / 16.0 if fwht else blocks).astype(np.float32)
+    for p in pay:
+        acc = (acc + _dequant_f32(*p)).astype(np.float32)
+    _check_quantised(got, acc.astype(np.float64))
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+def test_requantize_local_special_cases(fwht):
+    """No peers: the result is the local slice compressed.  An all-zero local
+    slice: the result equals the sum without one."""
+    xb = inputs.make_normal(5, 2048, seed=81)
+    alone = oracle.requantize([], local=xb, fwht=fwht)
+    comp = oracle.compress(xb, fwht=fwht)
+    for key in ("codes", "micro", "block"):
+        np.testing.assert_array_equal(alone[key], comp[key])
+    pay = _payloads(3, rows=5, L=2048, seed=83)
+    zero = np.zeros((5, 2048), np.uint16)
+    a = oracle.requantize(pay, local=zero, fwht=fwht)
+    b = oracle.requantize(pay)
+    for key in ("codes", "micro", "block"):
+        np.testing.assert_array_equal(a[key], b[key])
 
 
 def test_requantize_doubling_is_exact():
