@@ -70,6 +70,8 @@ def measured_traffic(path: str = None):
 
 
 def _short(kernel_name: str) -> str:
+    if "requantize_kernel<true" in kernel_name:
+        return "requantize_local"
     for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate", "requantize"):
         if fam + "_kernel" in kernel_name:
             return fam
@@ -85,7 +87,8 @@ REDUCE_K = 8
 def _receiver_bytes():
     n = REDUCE_N
     pay = n // 2 + n // 16 + n // 64
-    return {"accumulate": REDUCE_K * pay + 4 * n, "requantize": (REDUCE_K + 1) * pay}
+    return {"accumulate": REDUCE_K * pay + 4 * n, "requantize": (REDUCE_K + 1) * pay,
+            "requantize_local": REDUCE_K * pay + 2 * n}   # 7 payloads + local bf16 in, 1 out
 
 
 def _largest_grid(rows, grid_key):
@@ -127,7 +130,7 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> str:
     out = ["| kernel | workload | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) | algorithmic bytes | ratio |",
            "|---|---|---|---|---|---|---|"]
     traffic = {}
-    for k in ("compress", "decompress", "accumulate", "requantize"):
+    for k in ("compress", "decompress", "accumulate", "requantize", "requantize_local"):
         # only launches of the workload each figure is defined for (one thread per 64 elements)
         head = k in ("compress", "decompress")
         want_grid = (32768 * 4096 if head else REDUCE_N) // 64
@@ -154,7 +157,7 @@ def summarize_trace(trace_dir: str) -> str:
         rows += list(csv.DictReader(open(f)))
     groups = {}
     for r in rows:
-        m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel)",
+        m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel(?:<[^>]*>)?)",
                       r["Kernel_Name"])
         if not m:
             continue
@@ -172,9 +175,10 @@ def summarize_trace(trace_dir: str) -> str:
 
 def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
     """The receiver's kernels on the reduce workload (k = 8 peers of 4096 x 11008,
-    N(0, 1e-3)): fp4q_decompress_accumulate (fp32 out) and fp4q_reduce_requantize.
-    Three rotating copies of the payloads; HIP events around every launch; the
-    rate is taken from the median launch."""
+    N(0, 1e-3)): fp4q_decompress_accumulate (fp32 out), fp4q_reduce_requantize, and
+    fp4q_reduce_requantize with the rank's own slice added uncompressed (7 payloads
+    + 1 bf16 tensor).  Three rotating copies of the inputs; HIP events around every
+    launch; the rate is taken from the median launch."""
     k, rows, L = 8, 4096, 11008
     n = rows * L
     pay = []
@@ -184,13 +188,17 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
     sets = [pay] + [[tuple(t.clone() for t in q) for q in pay] for _ in range(2)]
     out = [torch.empty((rows, L), dtype=torch.float32, device=dev) for _ in range(3)]
     req = [fp4q.fp4q_reduce_requantize(pay) for _ in range(3)]
+    # an 8-rank slice with the rank's own part uncompressed: 7 payloads + the local bf16 tensor
+    loc = [torch.from_numpy(inputs.make_reduce_peer(k - 1).view(np.int16)).to(dev) for _ in range(3)]
     payload = n // 2 + n // 16 + n // 64
     res = {}
     for name, fn, nbytes in (
             ("decompress_accumulate", lambda i: fp4q.fp4q_decompress_accumulate(sets[i % 3], out=out[i % 3]),
              k * payload + 4 * n),
             ("reduce_requantize", lambda i: fp4q.fp4q_reduce_requantize(sets[i % 3], *req[i % 3]),
-             (k + 1) * payload)):
+             (k + 1) * payload),
+            ("reduce_requantize_local", lambda i: fp4q.fp4q_reduce_requantize(
+                sets[i % 3][:k - 1], *req[i % 3], local=loc[i % 3]), k * payload + 2 * n)):
         for i in range(6):
             fn(i)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
@@ -212,10 +220,12 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
                      "p90_us": round(float(np.percentile(t, 90)) * 1e6, 2),
                      "algorithmic_bytes": nbytes, "achieved_GBps": round(gbps, 1),
                      "frac": round(gbps / PEAK_GBPS, 4),
-                     "traffic": (measured_traffic(RECEIVER_TRAFFIC_SUMMARY) or {}).get(name.split("_")[-1])}
+                     "traffic": (measured_traffic(RECEIVER_TRAFFIC_SUMMARY) or {}).get(
+                         name.replace("decompress_", "").replace("reduce_", ""))}
         log("receiver %-22s median %7.1f us (avg %.1f, p90 %.1f)  %7.1f GB/s  %.1f%% of HBM peak" % (
             name, med * 1e6, t.mean() * 1e6, res[name]["p90_us"], gbps, 100 * gbps / PEAK_GBPS))
-    res["workload"] = "k=8 peers of bf16 4096x11008 N(0,1e-3), seeds 4..11"
+    res["workload"] = ("k=8 peers of bf16 4096x11008 N(0,1e-3), seeds 4..11; the _local entry sums "
+                       "peers 0..6 and adds peer 7's bf16 tensor uncompressed")
     return res
 
 

@@ -59,13 +59,14 @@ def lib() -> ctypes.CDLL:
         L.fp4q_decompress_accumulate.argtypes = [I, PP, PP, PP, I64, I64, P, I, P]
         L.fp4q_decompress_accumulate_ex.argtypes = [I, PP, PP, PP, I64, I64, P, I, U32, P]
         L.fp4q_reduce_requantize.argtypes = [I, PP, PP, PP, I64, I64, P, P, P, P]
+        L.fp4q_reduce_requantize_ex.argtypes = [I, PP, PP, PP, P, I64, I64, P, P, P, U32, P]
         L.fp4q_compress_mx.argtypes = [P, I64, I64, P, P, U32, P]
         L.fp4q_decompress_mx.argtypes = [P, P, I64, I64, P, I, U32, P]
         L.fp4q_status_str.argtypes = [I]
         L.fp4q_status_str.restype = ctypes.c_char_p
         for f in ("fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex", "fp4q_decompress",
                   "fp4q_decompress_ex", "fp4q_decompress_accumulate",
-                  "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize",
+                  "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize", "fp4q_reduce_requantize_ex",
                   "fp4q_compress_mx", "fp4q_decompress_mx"):
             getattr(L, f).restype = I
         _lib = L
@@ -169,14 +170,23 @@ def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 
 
 
 def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales=None,
-                           stream=None):
-    """Sum k peers' payloads [(codes, micro, block), ...] in the transform domain
-    and quantise the sum again -> (codes, micro, block) of the same shape."""
+                           local=None, flags: int = 0, stream=None):
+    """Sum k peers' payloads [(codes, micro, block), ...] in the transform domain,
+    starting from the transformed local bf16 slice when ``local`` is given, and
+    quantise the sum again -> (codes, micro, block) of the same shape."""
     import torch
     k = len(payloads)
-    rows, half = _dims(payloads[0][0]) if k else (0, 0)
-    L = 2 * half
-    dev = payloads[0][0].device
+    if k:
+        rows, half = _dims(payloads[0][0])
+        L = 2 * half
+        dev = payloads[0][0].device
+    elif local is not None:
+        rows, L = _dims(local)
+        dev = local.device
+    else:
+        raise ValueError("fp4q_reduce_requantize: needs a payload or a local slice")
+    if local is not None and local.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("fp4q_reduce_requantize: local must hold bf16 bit patterns")
     if codes is None:
         codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
     if micro_scales is None:
@@ -188,8 +198,9 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
     cs = PA(*[p[0].data_ptr() for p in payloads])
     ms = PA(*[p[1].data_ptr() for p in payloads])
     bs = PA(*[p[2].data_ptr() for p in payloads])
-    _check(lib().fp4q_reduce_requantize(k, cast(cs), cast(ms), cast(bs), rows, L, _ptr(codes),
-                                        _ptr(micro_scales), _ptr(block_scales), _stream(stream)))
+    _check(lib().fp4q_reduce_requantize_ex(
+        k, cast(cs), cast(ms), cast(bs), _ptr(local) if local is not None else None, rows, L,
+        _ptr(codes), _ptr(micro_scales), _ptr(block_scales), flags, _stream(stream)))
     return codes, micro_scales, block_scales
 
 

@@ -369,6 +369,33 @@ __device__ __forceinline__ void load_tile(const uint4 *__restrict__ in, int64_t 
     }
 }
 
+// The wavefront's bf16 tile staged through its LDS region (kStageChunks
+// chunks); each lane then reads its 128 contiguous bytes and widens them:
+// register j = element 64 q + j of block p (exact).
+__device__ __forceinline__ void load_widen(const Lane &L, const uint4 *__restrict__ in,
+                                           int64_t nblocks, uint4 *__restrict__ lds,
+                                           float (&R)[64]) {
+    {
+        uint4 d[8];
+        load_tile(in, L.tile, nblocks, L.lane, d);
+        uint4 *dst = lds + 33 * (L.lane >> 5) + (L.lane & 31);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[66 * j] = d[j];
+    }
+    wave_lds_sync();
+    const uint4 *srcl = lds + 33 * L.p + 8 * L.q;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 x = srcl[i];
+        const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            R[8 * i + 2 * k] = as_f(w[k] << 16);              // bf16 -> fp32, exact
+            R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+        }
+    }
+}
+
 template <bool kFwht>
 __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     const uint4 *__restrict__ in, int64_t nblocks, uint4 *__restrict__ codes,
@@ -376,33 +403,9 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     __shared__ uint4 lds_all[kSenderWaves * kStageChunks];
     const Lane L = lane_map<kSenderWaves>(nblocks);
     uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
-    const int lane = L.lane, p = L.p, q = L.q;
-    const int64_t tile = L.tile;
 
-    // stage the tile through LDS; each lane then reads its 128 contiguous bytes
-    {
-        uint4 d[8];
-        load_tile(in, tile, nblocks, lane, d);
-        uint4 *dst = lds + 33 * (lane >> 5) + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[66 * j] = d[j];
-    }
-    wave_lds_sync();
     float R[64];
-    {
-        const uint4 *srcl = lds + 33 * p + 8 * q;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 x = srcl[i];
-            const unsigned w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                R[8 * i + 2 * k] = as_f(w[k] << 16);              // bf16 -> fp32, exact
-                R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
-            }
-        }
-    }
-
+    load_widen(L, in, nblocks, lds, R);
     compress_transform<kFwht>(R);
 
     float s, t[4];
@@ -649,26 +652,62 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
 // ------------------------------------------- receiver-side re-quantisation
 // Reduce-scatter step of a compressed AllReduce: the k payloads of a slice are
 // summed where they live, in the transform domain (rounded products added in
-// peer order to an accumulator that starts at +0), and the sum is quantised
-// again with the compress steps -- no transform is needed, since decompressing,
-// summing and compressing would apply the self-inverse H / 16 twice.
+// peer order), and the sum is quantised again with the compress steps -- no
+// inverse transform is needed, since decompressing, summing and compressing
+// would apply the self-inverse H / 16 twice.  The accumulator starts at +0, or
+// (kLocal) at the rank's own uncompressed part of the slice, transformed as
+// compress transforms its input.
 // Register j of quarter q holds element 32 q + 128 (j >> 5) + (j & 31), so
 // register group k = j >> 4 is micro-group (k & 1) + 2 q + 8 (k >> 1), and code
 // dwords 0-3 / 4-7 are the block's 16-byte chunks q / q + 4.
-__global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
-    Peers peers, int k, int64_t nblocks, uint4 *__restrict__ codes,
-    unsigned short *__restrict__ micro, float *__restrict__ block) {
-    __shared__ uint4 lds[kReceiverWaves * 144];
-    const Lane L = lane_map<kReceiverWaves>(nblocks);
-    float R[64];
+// The local tile arrives as register j = element 64 q + j (index bits 0-5 in
+// the register, 6 and 7 in lane bits 4 and 5); butterflies on index bits 0-5,
+// then two exchanges through register bit 5 bring index bit 6 in (and 5 out to
+// lane bit 4), then bit 7 in (and 6 out to lane bit 5): the layout above, with
+// the butterflies in ascending index-bit order.
+template <bool kFwht>
+__device__ __forceinline__ void local_transform(float (&R)[64]) {
+    if constexpr (kFwht) {
+        stage<1>(R);
+        stage<2>(R);
+        stage<4>(R);
+        stage<8>(R);
+        stage<16>(R);
+        stage<32>(R);
+    }
+    swap_lane4<32>(R);
+    if constexpr (kFwht) stage<32>(R);  // index bit 6
+    swap_lane5<32>(R);
+    if constexpr (kFwht) {
+        stage<32>(R);  // index bit 7
 #pragma unroll
-    for (int j = 0; j < 64; ++j) R[j] = 0.0f;
+        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+    }
+}
+
+template <bool kLocal, bool kFwht>
+__global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
+    Peers peers, int k, const uint4 *__restrict__ local, int64_t nblocks,
+    uint4 *__restrict__ codes, unsigned short *__restrict__ micro, float *__restrict__ block) {
+    constexpr int kChunks = kLocal ? kStageChunks : 144;
+    __shared__ uint4 lds_all[kReceiverWaves * kChunks];
+    const Lane L = lane_map<kReceiverWaves>(nblocks);
+    uint4 *lds = lds_all + (threadIdx.x / kWave) * kChunks;
+    float R[64];
+    if constexpr (kLocal) {
+        load_widen(L, local, nblocks, lds, R);
+        local_transform<kFwht>(R);
+        wave_lds_sync();  // every lane has read its input chunks
+    } else {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) R[j] = 0.0f;
+    }
     sum_peers<kAdd>(L, peers, k, R);
 
     float s, t[4];
     unsigned mw, C[8];
     quantize_groups<false>(R, s, t, mw, C);
-    store_codes(L, nblocks, lds + (threadIdx.x / kWave) * 144, codes, C);
+    store_codes(L, nblocks, lds, codes, C);
     if (L.valid) {
         micro[L.b * 8 + L.q] = (unsigned short)(mw & 0xFFFFu);  // groups 2q, 2q + 1
         micro[L.b * 8 + 4 + L.q] = (unsigned short)(mw >> 16);  // groups 2q + 8, 2q + 9
@@ -963,19 +1002,27 @@ int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,
                                          out_dtype, 0u, stream);
 }
 
-int fp4q_reduce_requantize(int k, const uint8_t *const *codes, const uint8_t *const *micro_scales,
-                           const float *const *block_scales, int64_t rows, int64_t row_len,
-                           uint8_t *out_codes, uint8_t *out_micro, float *out_block,
-                           void *stream) {
+int fp4q_reduce_requantize_ex(int k, const uint8_t *const *codes,
+                              const uint8_t *const *micro_scales,
+                              const float *const *block_scales, const uint16_t *local_bf16,
+                              int64_t rows, int64_t row_len, uint8_t *out_codes,
+                              uint8_t *out_micro, float *out_block, uint32_t flags,
+                              void *stream) {
     int64_t n, nb;
     int st = check_shape(rows, row_len, &n, &nb);
     if (st != FP4Q_OK) return st;
-    if (k < 1 || k > FP4Q_MAX_PEERS) return FP4Q_ERR_K;
+    if (k < (local_bf16 ? 0 : 1) || k > FP4Q_MAX_PEERS) return FP4Q_ERR_K;
+    if (flags & ~(uint32_t)FP4Q_FLAG_NO_FWHT) return FP4Q_ERR_ARG;
     if (n == 0) return FP4Q_OK;
-    if (!codes || !micro_scales || !block_scales) return FP4Q_ERR_NULL;
+    if (k > 0 && (!codes || !micro_scales || !block_scales)) return FP4Q_ERR_NULL;
     if ((st = check_payload_ptrs(out_codes, out_micro, out_block)) != FP4Q_OK) return st;
+    if (local_bf16 && !aligned(local_bf16, 16)) return FP4Q_ERR_ALIGN;
     const Range oc = rng(out_codes, n / 2), om = rng(out_micro, n / 16), ob = rng(out_block, 4 * nb);
     if (overlap(oc, om) || overlap(oc, ob) || overlap(om, ob)) return FP4Q_ERR_ARG;
+    if (local_bf16) {
+        const Range il = rng(local_bf16, 2 * n);
+        if (overlap(oc, il) || overlap(om, il) || overlap(ob, il)) return FP4Q_ERR_ARG;
+    }
     Peers peers = {};
     for (int p = 0; p < k; ++p) {
         if ((st = check_payload_ptrs(codes[p], micro_scales[p], block_scales[p])) != FP4Q_OK)
@@ -988,8 +1035,20 @@ int fp4q_reduce_requantize(int k, const uint8_t *const *codes, const uint8_t *co
         peers.micro[p] = reinterpret_cast<const uint4 *>(micro_scales[p]);
         peers.block[p] = block_scales[p];
     }
-    void *args[] = {&peers, &k, &nb, &out_codes, &out_micro, &out_block};
-    return launch((const void *)&requantize_kernel, nb, kReceiverWaves, args, stream);
+    void *args[] = {&peers, &k, &local_bf16, &nb, &out_codes, &out_micro, &out_block};
+    const bool fw = !(flags & FP4Q_FLAG_NO_FWHT);
+    const void *fn = !local_bf16 ? (const void *)&requantize_kernel<false, true>
+                     : fw        ? (const void *)&requantize_kernel<true, true>
+                                 : (const void *)&requantize_kernel<true, false>;
+    return launch(fn, nb, kReceiverWaves, args, stream);
+}
+
+int fp4q_reduce_requantize(int k, const uint8_t *const *codes, const uint8_t *const *micro_scales,
+                           const float *const *block_scales, int64_t rows, int64_t row_len,
+                           uint8_t *out_codes, uint8_t *out_micro, float *out_block,
+                           void *stream) {
+    return fp4q_reduce_requantize_ex(k, codes, micro_scales, block_scales, nullptr, rows, row_len,
+                                     out_codes, out_micro, out_block, 0u, stream);
 }
 
 int fp4q_compress_mx(const uint16_t *in_bf16, int64_t rows, int64_t row_len, uint8_t *codes,

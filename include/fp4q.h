@@ -141,6 +141,23 @@ int fp4q_reduce_requantize(int k, const uint8_t *const *codes,
                            uint8_t *out_codes, uint8_t *out_micro, float *out_block,
                            void *stream);
 
+/* The same step with the rank's own part of the slice added uncompressed (the
+ * fused decompress-accumulate, add-local, re-compress of that AllReduce):
+ * the accumulator starts at local_bf16 transformed exactly as fp4q_compress
+ * transforms its input (as is with FP4Q_FLAG_NO_FWHT, matching payloads
+ * compressed with that flag), then the k peers' terms are added as above.
+ *   local_bf16  bf16 [rows, row_len], 16-byte aligned, or NULL (then this is
+ *     fp4q_reduce_requantize); must not overlap the outputs
+ *   k           0 <= k <= FP4Q_MAX_PEERS with a local slice (k = 0 gives
+ *     exactly fp4q_compress(local_bf16)), 1 <= k without one
+ *   flags       0 or FP4Q_FLAG_NO_FWHT */
+int fp4q_reduce_requantize_ex(int k, const uint8_t *const *codes,
+                              const uint8_t *const *micro_scales,
+                              const float *const *block_scales, const uint16_t *local_bf16,
+                              int64_t rows, int64_t row_len, uint8_t *out_codes,
+                              uint8_t *out_micro, float *out_block, uint32_t flags,
+                              void *stream);
+
 /* MXFP4-style variant: the microscaling FP4 format (blocks of 32, E2M1
  * elements) named on the gist.science page ("Practical FP4 Training for
  * Large-Scale MoE Models on Hopper GPUs", Problemstellung item 2), applied

@@ -24,6 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["fp4q_payload_bytes", "fp4q_compress", "fp4q_compress_ex",
                             "fp4q_decompress", "fp4q_decompress_ex", "fp4q_decompress_accumulate",
                             "fp4q_decompress_accumulate_ex", "fp4q_reduce_requantize",
+                            "fp4q_reduce_requantize_ex",
                             "fp4q_compress_mx", "fp4q_decompress_mx", "fp4q_status_str"])
     for n in names:
         assert hasattr(L, n), n
@@ -143,6 +144,34 @@ def test_requantize_validation_order():
     assert req(1, cs, [A + big + 4], bs, 1, 256, *outs) == fp4q.FP4Q_ERR_ALIGN
     assert req(1, cs, ms, bs, 4, 256, A + 16, outs[1], outs[2]) == fp4q.FP4Q_ERR_ARG   # over input codes
     assert req(1, cs, ms, bs, 4, 256, outs[0], outs[0] + 16, outs[2]) == fp4q.FP4Q_ERR_ARG
+
+
+def req_ex(k, cs, ms, bs, local, rows, L, oc, om, ob, flags=0):
+    PA = ctypes.c_void_p * max(len(cs), 1)
+    cast = lambda a: ctypes.cast(PA(*a), ctypes.POINTER(ctypes.c_void_p))
+    return fp4q.lib().fp4q_reduce_requantize_ex(k, cast(cs), cast(ms), cast(bs), local, rows, L,
+                                                oc, om, ob, flags, None)
+
+
+def test_requantize_ex_validation_order():
+    big = 1 << 30
+    cs, ms, bs = [A], [A + big], [A + 2 * big]
+    outs = (A + 3 * big, A + 4 * big, A + 5 * big)
+    local = A + 6 * big
+    assert req_ex(1, cs, ms, bs, local, 1, 100, *outs) == fp4q.FP4Q_ERR_SHAPE
+    assert req_ex(0, [], [], [], NULL, 1, 256, *outs) == fp4q.FP4Q_ERR_K      # k = 0 needs local
+    assert req_ex(-1, [], [], [], local, 1, 256, *outs) == fp4q.FP4Q_ERR_K
+    assert req_ex(17, cs * 17, ms * 17, bs * 17, local, 1, 256, *outs) == fp4q.FP4Q_ERR_K
+    assert req_ex(1, cs, ms, bs, local, 1, 256, *outs, flags=2) == fp4q.FP4Q_ERR_ARG
+    assert req_ex(0, [], [], [], local, 0, 256, *outs) == fp4q.FP4Q_OK        # empty: no launch
+    assert req_ex(0, [], [], [], local, 1, 256, NULL, outs[1], outs[2]) == fp4q.FP4Q_ERR_NULL
+    assert req_ex(2, cs + [NULL], ms * 2, bs * 2, local, 1, 256, *outs) == fp4q.FP4Q_ERR_NULL
+    assert req_ex(0, [], [], [], local + 8, 1, 256, *outs) == fp4q.FP4Q_ERR_ALIGN
+    assert req_ex(1, cs, ms, bs, local, 1, 256, outs[0], outs[1] + 4, outs[2]) == fp4q.FP4Q_ERR_ALIGN
+    # local slice over an output, or an output over the local slice
+    assert req_ex(0, [], [], [], outs[0], 4, 256, *outs) == fp4q.FP4Q_ERR_ARG
+    assert req_ex(0, [], [], [], local, 4, 256, local + 256, outs[1], outs[2]) == fp4q.FP4Q_ERR_ARG
+    assert req_ex(1, cs, ms, bs, local, 4, 256, A + 16, outs[1], outs[2]) == fp4q.FP4Q_ERR_ARG
 
 
 def test_mx_validation_order():

@@ -352,3 +352,53 @@ def test_offsets_beyond_32_bits(fp4q):
     assert n > (1 << 32)
     del acc, acc_bf, out, c, m, b
     torch.cuda.empty_cache()
+
+
+def _requantize_local_case(fp4q, peers_b, local_b, fwht, name):
+    _say("requantize+local %s k=%d shape %s fwht %s" % (name, len(peers_b), local_b.shape, fwht))
+    flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+    trip = [(r["codes"], r["micro"], r["block"])
+            for r in (oracle.compress(p, fwht=fwht) for p in peers_b)]
+    ref = oracle.requantize(trip, debug=True, local=local_b, fwht=fwht)
+    out = fp4q.fp4q_reduce_requantize([tuple(to_dev(a) for a in t) for t in trip],
+                                      local=to_dev(local_b), flags=flags)
+    torch.cuda.synchronize()
+    return parity.check_compress([o.cpu().numpy() for o in out], ref)
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+@pytest.mark.parametrize("k,rows,L", [(0, 37, 4096), (1, 4, 256), (3, 5, 11008), (8, 64, 4096),
+                                      (16, 9, 2048)])
+def test_requantize_local_parity(fp4q, k, rows, L, fwht):
+    """The rank's own bf16 slice added uncompressed, then k peers' payloads."""
+    peers = [inputs.make_normal(rows, L, seed=400 + p, scale=1e-3) for p in range(k)]
+    local = inputs.make_normal(rows, L, seed=450, scale=1e-3)
+    st = _requantize_local_case(fp4q, peers, local, fwht, "%dx%d" % (rows, L))
+    assert st["code_mismatch"] == 0 and st["micro_mismatch"] == 0
+
+
+def test_requantize_local_edge_cases(fp4q):
+    peers = [inputs.make_edge_case("tiny", 12, 1024, seed=500 + p) for p in range(2)]
+    for kind in ("mixed_blocks", "huge", "zeros", "spike"):
+        local = inputs.make_edge_case(kind, 12, 1024, seed=510)
+        _requantize_local_case(fp4q, peers, local, True, "edge-" + kind)
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+def test_requantize_local_alone_is_compress(fp4q, fwht):
+    """With no peers the re-quantised local slice is exactly its compressed payload."""
+    flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+    x = to_dev(inputs.make_config("outlier8192", rows=300))
+    a = fp4q.fp4q_reduce_requantize([], local=x, flags=flags)
+    b = fp4q.fp4q_compress(x, flags=flags)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+
+
+def test_requantize_local_full_size(fp4q):
+    """An 8-rank slice: 7 received payloads of 4096 x 11008 plus the rank's own
+    uncompressed part (the eighth tensor of the reduce workload)."""
+    peers = [inputs.make_reduce_peer(p) for p in range(7)]
+    st = _requantize_local_case(fp4q, peers, inputs.make_reduce_peer(7), True, "reduce-k7+local")
+    _say("  %s" % st)
