@@ -232,7 +232,9 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
 def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
     """Throughput and relative RMSE with and without the transform on the activation
     (2048x4096) and outlier (8192x4096) workloads.  These tensors fit in the 256 MB
-    last-level cache, so their rates are cache-resident, not HBM roofline figures."""
+    last-level cache, so their rates are cache-resident, not HBM roofline figures.
+    Times are GPU time per compress + decompress, from a HIP graph of `iters`
+    steps replayed 5 times."""
     rows_out = []
     for name in ("act2048", "outlier8192"):
         xb = inputs.make_config(name)
@@ -257,11 +259,27 @@ def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
             for _ in range(5):
                 once()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(iters):
-                once()
+            # GPU time per step: `iters` steps captured in one HIP graph, replayed
+            # (on tensors this small the Python calls would otherwise dominate)
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for _ in range(iters):
+                        once()
+            torch.cuda.current_stream().wait_stream(side)
+            g.replay()
             torch.cuda.synchronize()
-            dt = (time.perf_counter() - t0) / iters
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            dt = e0.elapsed_time(e1) * 1e-3 / (reps * iters)
+            del g
             rmse = float(torch.linalg.vector_norm(Y.double() - xf) / torch.linalg.vector_norm(xf))
             rows_out.append({"workload": name, "transform": label, "us_per_step": round(dt * 1e6, 1),
                              "GBps_bf16_in": round(2 * x.numel() / dt / 1e9, 1),

@@ -107,14 +107,59 @@ def _dims(x):
     return int(x.shape[0]), int(x.shape[1])
 
 
+_BF16_BITS = ("bfloat16", "int16", "uint16")
+_DTYPES = {}
+
+
+def _dtypes(names):
+    """The torch dtypes named (cached: the check runs on every call)."""
+    d = _DTYPES.get(names)
+    if d is None:
+        import torch
+        d = _DTYPES[names] = frozenset(getattr(torch, n) for n in names)
+    return d
+
+
+def _arg(t, name, numel, dtypes):
+    """Check one tensor argument before its address goes to the library, which
+    sees only pointers: its type, element type, contiguity and element count (a
+    buffer too small or strided would otherwise be read or written out of bounds
+    by a kernel).  _on_gpu checks the devices afterwards."""
+    try:
+        ok = t.dtype in _dtypes(dtypes)
+    except AttributeError:
+        raise TypeError("fp4q: %s must be a torch tensor" % name) from None
+    if not ok:
+        raise TypeError("fp4q: %s must be %s, got %s" % (name, " or ".join(dtypes), t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("fp4q: %s must be contiguous" % name)
+    if t.numel() != numel:
+        raise ValueError("fp4q: %s must hold %d elements, has %d" % (name, numel, t.numel()))
+    return t
+
+
+def _on_gpu(*tensors):
+    """Every tensor argument in device memory, all on the same GPU."""
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("fp4q: every tensor must be on the same GPU (%s, %s)" % (dev, t.device))
+
+
+def _payload_args(codes, micro, block, n, who):
+    _arg(codes, who + " codes", n // 2, ("uint8",))
+    _arg(micro, who + " micro-scales", n // FP4Q_GROUP, ("uint8",))
+    _arg(block, who + " block scales", n // FP4Q_BLOCK, ("float32",))
+    return [codes, micro, block]
+
+
 def fp4q_compress(x, codes=None, micro_scales=None, block_scales=None, flags: int = 0,
                   stream=None):
     """bf16 [rows, row_len] (CUDA) -> (codes u8 [rows, L/2], micro u8 [rows, L/16],
     block f32 [rows, L/256]).  Output tensors are allocated when not given."""
     import torch
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError("fp4q_compress: input must hold bf16 bit patterns")
     rows, L = _dims(x)
+    _arg(x, "input", rows * L, _BF16_BITS)
     dev = x.device
     if codes is None:
         codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
@@ -122,6 +167,7 @@ def fp4q_compress(x, codes=None, micro_scales=None, block_scales=None, flags: in
         micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
     if block_scales is None:
         block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
+    _on_gpu(x, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
     _check(lib().fp4q_compress_ex(_ptr(x), rows, L, _ptr(codes), _ptr(micro_scales),
                                   _ptr(block_scales), flags, _stream(stream)))
     return codes, micro_scales, block_scales
@@ -142,8 +188,10 @@ def fp4q_decompress(codes, micro_scales, block_scales, out=None, out_dtype=None,
     import torch
     rows, half = _dims(codes)
     L = 2 * half
+    pay = _payload_args(codes, micro_scales, block_scales, rows * L, "payload")
     if out is None:
         out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
+    _on_gpu(*pay, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     _check(lib().fp4q_decompress_ex(_ptr(codes), _ptr(micro_scales), _ptr(block_scales), rows, L,
                                     _ptr(out), _out_dtype_code(out.dtype), flags, _stream(stream)))
     return out
@@ -153,11 +201,17 @@ def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 
     """Sum of k peers' payloads [(codes, micro, block), ...] -> float32 (or bf16)."""
     import torch
     k = len(payloads)
-    rows, half = _dims(payloads[0][0]) if k else (0, 0)
+    if not 1 <= k <= FP4Q_MAX_PEERS:
+        raise Fp4qError(FP4Q_ERR_K)
+    rows, half = _dims(payloads[0][0])
     L = 2 * half
+    dev = payloads[0][0].device
+    ins = []
+    for i, (c, m, b) in enumerate(payloads):
+        ins += _payload_args(c, m, b, rows * L, "peer %d" % i)
     if out is None:
-        out = torch.empty((rows, L), dtype=out_dtype or torch.float32,
-                          device=payloads[0][0].device)
+        out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=dev)
+    _on_gpu(*ins, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     PA = ctypes.c_void_p * max(k, 1)
     cs = PA(*[p[0].data_ptr() for p in payloads])
     ms = PA(*[p[1].data_ptr() for p in payloads])
@@ -176,23 +230,27 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
     quantise the sum again -> (codes, micro, block) of the same shape."""
     import torch
     k = len(payloads)
+    if k > FP4Q_MAX_PEERS or (k == 0 and local is None):
+        raise Fp4qError(FP4Q_ERR_K)
     if k:
         rows, half = _dims(payloads[0][0])
         L = 2 * half
         dev = payloads[0][0].device
-    elif local is not None:
+    else:
         rows, L = _dims(local)
         dev = local.device
-    else:
-        raise ValueError("fp4q_reduce_requantize: needs a payload or a local slice")
-    if local is not None and local.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError("fp4q_reduce_requantize: local must hold bf16 bit patterns")
+    ins = []
+    for i, (c, m, b) in enumerate(payloads):
+        ins += _payload_args(c, m, b, rows * L, "peer %d" % i)
+    if local is not None:
+        ins.append(_arg(local, "local slice", rows * L, _BF16_BITS))
     if codes is None:
         codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
     if micro_scales is None:
         micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
     if block_scales is None:
         block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
+    _on_gpu(*ins, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
     PA = ctypes.c_void_p * max(k, 1)
     cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
     cs = PA(*[p[0].data_ptr() for p in payloads])
@@ -207,24 +265,29 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
 def fp4q_compress_mx(x, codes=None, scales=None, flags: int = 0, stream=None):
     """MXFP4-style: bf16 [rows, L] -> (codes u8 [rows, L/2], E8M0 scales u8 [rows, L/32])."""
     import torch
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError("fp4q_compress_mx: input must hold bf16 bit patterns")
     rows, L = _dims(x)
+    _arg(x, "input", rows * L, _BF16_BITS)
     if codes is None:
         codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, L // 32), dtype=torch.uint8, device=x.device)
+    _on_gpu(x, _arg(codes, "output codes", rows * L // 2, ("uint8",)),
+            _arg(scales, "output scales", rows * L // 32, ("uint8",)))
     _check(lib().fp4q_compress_mx(_ptr(x), rows, L, _ptr(codes), _ptr(scales), flags,
                                   _stream(stream)))
     return codes, scales
 
 
 def fp4q_decompress_mx(codes, scales, out=None, out_dtype=None, flags: int = 0, stream=None):
+    """MXFP4-style payload -> [rows, row_len] float32 (or bfloat16)."""
     import torch
     rows, half = _dims(codes)
     L = 2 * half
+    _arg(codes, "codes", rows * L // 2, ("uint8",))
+    _arg(scales, "scales", rows * L // 32, ("uint8",))
     if out is None:
         out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
+    _on_gpu(codes, scales, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     _check(lib().fp4q_decompress_mx(_ptr(codes), _ptr(scales), rows, L, _ptr(out),
                                     _out_dtype_code(out.dtype), flags, _stream(stream)))
     return out
