@@ -53,7 +53,12 @@ def algorithmic_bytes(n: int):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and white space removed, so that
+    counter summaries stay attached to the code they measured, not its prose."""
+    text = open(KERNEL_SOURCE).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
 def measured_traffic(path: str = None):

@@ -5,7 +5,10 @@
 // LLM Training" (abstract): a hybrid two-level fast Walsh-Hadamard transform,
 // micro-grouped dual-scale FP4 quantisation and cooperative FP4 packing on the
 // sender; dequantisation, the inverse transform and (zot.news digest, "Read it
-// as": the AllReduce of tensor parallelism) the sum of k peers on the receiver.
+// as": the AllReduce of tensor parallelism) the sum of k peers on the receiver,
+// or that sum (plus the rank's own uncompressed slice) quantised again for the
+// all-gather half of the AllReduce.  A microscaling variant (32-element groups,
+// power-of-two scales) sits beside the dual scale.
 //
 // Work mapping: one wavefront (64 lanes) handles a tile of 16 blocks of 256
 // elements; lane l works on block p = l & 15 of the tile, together with the
@@ -19,12 +22,15 @@
 // register bit by v_permlane16_swap (lane bit 4) or v_permlane32_swap (lane bit
 // 5), one instruction per register pair, and then transformed in registers.
 // The order of these exchanges is chosen per kernel so that
-//   * every 16-byte global access of the four quarters covers whole 64-byte
-//     segments (loads use the non-temporal path; stores are only full-rate when
-//     an instruction writes whole segments),
+//   * the receiver's payload loads of the four quarters cover whole 64-byte
+//     segments per instruction (non-temporal path),
 //   * compress ends with four whole micro-groups per lane, so group maxima,
-//     scales, quantisation and packing stay in registers.
-// No LDS and no MFMA: the work is streaming and the transform is butterflies.
+//     scales, quantisation and packing stay in registers,
+//   * the receiver ends with 16-byte register quads of contiguous output.
+// LDS only re-deals data between that lane-local layout and fully coalesced
+// 1 KiB-per-instruction global accesses (the bf16 input tile, the codes and the
+// output), in a region private to each wavefront.  No MFMA: the work is
+// streaming and the transform is butterflies.
 //
 // Numerics follow the method's fp32 operation order exactly (built with
 // -ffp-contract=off, IEEE division, fp32 denormals kept):
@@ -444,7 +450,6 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
 // bits 0-4 = index bits 0-4, bit 5 = index bit 7; lane bits 4, 5 = index bits
 // 5, 6.  Its micro-group is (j >> 4 & 1) + 2 q + 8 h, so register group j >> 4
 // uses micro byte 2 q + (j >> 4 & 1) + 8 (j >> 5).
-// With kFma the dequantised values are added into R (receiver-side sum).
 // One lane's part of a payload: 32 code bytes, two micro-scale pairs, the block scale.
 struct PayloadRegs {
     uint4 c0, c1;
