@@ -229,6 +229,42 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
                          name.replace("decompress_", "").replace("reduce_", ""))}
         log("receiver %-22s median %7.1f us (avg %.1f, p90 %.1f)  %7.1f GB/s  %.1f%% of HBM peak" % (
             name, med * 1e6, t.mean() * 1e6, res[name]["p90_us"], gbps, 100 * gbps / PEAK_GBPS))
+    # One rank's GPU work in an 8-rank compressed AllReduce (two exchanges): compress
+    # its whole partial tensor, re-quantise its 1/8 row-slice from the 7 received
+    # payload slices plus its own uncompressed slice, decompress the gathered payload.
+    per = rows // k
+    Xs = loc
+    Ps = [tuple(torch.empty_like(t) for t in pay[0]) for _ in range(3)]
+    Rs = [tuple(t[:per].clone() for t in pay[0]) for _ in range(3)]
+    Ys = out
+
+    def rank_step(i):
+        s = i % 3
+        fp4q.fp4q_compress(Xs[s], *Ps[s])
+        fp4q.fp4q_reduce_requantize([tuple(t[:per] for t in q) for q in sets[s][:k - 1]], *Rs[s],
+                                    local=Xs[s][:per])
+        fp4q.fp4q_decompress(*sets[s][k - 1], out=Ys[s])
+    for i in range(6):
+        rank_step(i)
+    torch.cuda.synchronize()
+    for i in range(8):
+        rank_step(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        rank_step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    nbytes = (2 * n + payload) + ((k - 1) * payload // k + 2 * n // k + payload // k) + (payload + 4 * n)
+    med = float(np.median(t))
+    res["allreduce_rank"] = {"median_us": round(med * 1e6, 2), "algorithmic_bytes": nbytes,
+                             "achieved_GBps": round(nbytes / med / 1e9, 1),
+                             "frac": round(nbytes / med / 1e9 / PEAK_GBPS, 4),
+                             "what": "compress 4096x11008 + re-quantise a 512-row slice (7 payload "
+                                     "slices + local) + decompress 4096x11008 (fp32)"}
+    log("receiver %-22s median %7.1f us  (one rank's kernels of an 8-rank compressed AllReduce)" % (
+        "allreduce_rank", med * 1e6))
     res["workload"] = ("k=8 peers of bf16 4096x11008 N(0,1e-3), seeds 4..11; the _local entry sums "
                        "peers 0..6 and adds peer 7's bf16 tensor uncompressed")
     return res

@@ -402,3 +402,40 @@ def test_requantize_local_full_size(fp4q):
     peers = [inputs.make_reduce_peer(p) for p in range(7)]
     st = _requantize_local_case(fp4q, peers, inputs.make_reduce_peer(7), True, "reduce-k7+local")
     _say("  %s" % st)
+
+
+def test_two_exchange_allreduce_emulated(fp4q):
+    """The compressed AllReduce of tensor parallelism, as the library's calls compose
+    it, for 8 ranks emulated on one GPU: every rank compresses its partial tensor;
+    rank j receives row-slice j of the 7 other payloads (payload arrays are
+    row-major, so a row-slice is a contiguous view) and re-quantises their sum
+    plus its own uncompressed slice; every rank then decompresses the 8 reduced
+    slices.  The GPU result equals the same composition through the oracle bit for
+    bit, and stays within FP4 error of the exact sum."""
+    ranks, rows, L = 8, 64, 4096
+    per = rows // ranks
+    xs = [inputs.make_normal(rows, L, seed=700 + r, scale=1e-3) for r in range(ranks)]
+    # GPU
+    xd = [to_dev(x) for x in xs]
+    pays = [fp4q.fp4q_compress(x) for x in xd]
+    sl = lambda t, j: t[j * per:(j + 1) * per]
+    reduced = [fp4q.fp4q_reduce_requantize(
+        [tuple(sl(t, j) for t in pays[r]) for r in range(ranks) if r != j], local=sl(xd[j], j))
+        for j in range(ranks)]
+    out = torch.cat([fp4q.fp4q_decompress(*p) for p in reduced])
+    torch.cuda.synchronize()
+    # oracle, same composition
+    opay = [oracle.compress(x) for x in xs]
+    osl = lambda d, j: tuple(d[k][j * per:(j + 1) * per] for k in ("codes", "micro", "block"))
+    ored = [oracle.requantize([osl(opay[r], j) for r in range(ranks) if r != j],
+                              local=xs[j][j * per:(j + 1) * per]) for j in range(ranks)]
+    want = np.concatenate([oracle.decompress(p["codes"], p["micro"], p["block"]) for p in ored])
+    for j in range(ranks):
+        for got, key in zip(reduced[j], ("codes", "micro", "block")):
+            assert np.array_equal(got.cpu().numpy().view(np.uint8), ored[j][key].view(np.uint8)), (j, key)
+    o = out.cpu().numpy()
+    np.testing.assert_array_equal(o.view(np.uint32), want.view(np.uint32))
+    exact = sum(inputs.bf16_bits_to_f32(x).astype(np.float64) for x in xs)
+    rel = np.linalg.norm(o - exact) / np.linalg.norm(exact)
+    _say("  emulated 8-rank compressed AllReduce: relative error %.4f" % rel)
+    assert rel < 0.25
