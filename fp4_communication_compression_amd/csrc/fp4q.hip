@@ -123,18 +123,37 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
-// 16-byte store on the non-temporal path.
-#ifndef FP4Q_RECEIVER_STORE_NT
-#define FP4Q_RECEIVER_STORE_NT 1
-#endif
-__device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
-#if FP4Q_RECEIVER_STORE_NT
-    const u32x4 t = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
-#else
-    *p = v;
-#endif
-}
+// Global stores.  Every kernel writes through buffer stores with the
+// system-scope cache policy (sc1): on this GPU they wrote streaming output about
+// 20 % faster than non-temporal global stores (6.1 against 4.9 TB/s on the
+// decompress traffic pattern, 6.95 against 6.5 on the compress pattern).  A
+// wavefront's descriptor covers exactly its tile's part of one output array
+// (the bytes of its valid blocks, so a store past the last block would also be
+// dropped by the hardware range check; the kernels do not issue any).
+constexpr int kStorePolicy = 16;  // sc1
+struct TileStore {
+    __amdgpu_buffer_rsrc_t r;
+    // bytes_per_block of the array, for the tile's blocks [tile, tile + 16) that exist
+    __device__ __forceinline__ TileStore(void *base, int64_t tile, int64_t nblocks,
+                                         int bytes_per_block) {
+        const int64_t nvalid = nblocks - tile < kTileBlocks ? nblocks - tile : kTileBlocks;
+        r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(base) + tile * bytes_per_block, 0,
+                                              static_cast<int>(nvalid * bytes_per_block), 0x00020000);
+    }
+    __device__ __forceinline__ void b128(int byte_offset, uint4 v) const {
+        const u32x4 t = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(t, r, byte_offset, 0, kStorePolicy);
+    }
+    __device__ __forceinline__ void b32(int byte_offset, unsigned v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_offset, 0, kStorePolicy);
+    }
+    __device__ __forceinline__ void b16(int byte_offset, unsigned short v) const {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, byte_offset, 0, kStorePolicy);
+    }
+    __device__ __forceinline__ void b8(int byte_offset, unsigned char v) const {
+        __builtin_amdgcn_raw_buffer_store_b8(v, r, byte_offset, 0, kStorePolicy);
+    }
+};
 
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
 __device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
@@ -348,11 +367,12 @@ __device__ __forceinline__ void store_codes(const Lane &L, int64_t nblocks, uint
     lds[9 * L.p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
     wave_lds_sync();
     const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
+    const TileStore out(codes, L.tile, nblocks, 128);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int64_t blk = L.tile + 8 * u + (lane >> 3);
+        const int b = 8 * u + (lane >> 3);  // block within the tile
         const uint4 v = srcl[72 * u];
-        if (blk < nblocks) codes[blk * 8 + (lane & 7)] = v;
+        if (L.tile + b < nblocks) out.b128(16 * (8 * b + (lane & 7)), v);
     }
 }
 
@@ -438,8 +458,8 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     wave_lds_sync();  // every lane has read its input chunks
     store_codes(L, nblocks, lds, codes, C);
     if (L.valid) {
-        micro[L.b * 4 + L.q] = mw;
-        if (L.q == 0) block[L.b] = s;
+        TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, mw);
+        if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, as_u(s));
     }
 }
 
@@ -538,14 +558,13 @@ __device__ __forceinline__ void receiver_transform(float (&R)[64]) {
 
 // Output staging: every lane's values go through the wave-private LDS region so
 // that each global store instruction writes 1 KiB of contiguous output (64
-// lanes x 16 bytes), the pattern the memory system absorbs fastest; stores take
-// the non-temporal path.
+// lanes x 16 bytes), the pattern the memory system absorbs fastest (stores with
+// the sc1 policy, TileStore).
 template <bool kBf16>
 __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
                                           void *__restrict__ out, const float (&R)[64]) {
     const int lane = L.lane, p = L.p;
     const int64_t tile = L.tile;
-    uint4 *o = reinterpret_cast<uint4 *>(out);
     if constexpr (kBf16) {
         // a block is 32 chunks of 8 bf16 (stride 33); register 8v + t is chunk q + 4v
         uint4 *dst = lds + 33 * p + L.q;
@@ -558,16 +577,18 @@ __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 
         }
         wave_lds_sync();
         const uint4 *src = lds + 33 * (lane >> 5) + (lane & 31);
+        const TileStore dst_g(out, tile, nblocks, 512);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {  // blocks 2u, 2u + 1 of the tile
-            const int64_t blk = tile + 2 * u + (lane >> 5);
+            const int b = 2 * u + (lane >> 5);
             const uint4 v = src[66 * u];
-            if (blk < nblocks) store_nt(o + blk * 32 + (lane & 31), v);
+            if (tile + b < nblocks) dst_g.b128(16 * (32 * b + (lane & 31)), v);
         }
     } else {
         // a block is 64 chunks of 4 fp32 (stride 65); register quad v holds chunk
         // q + 8 (v & 1) + 16 (v >> 1 & 1) + 4 (v >> 2 & 1) + 32 (v >> 3).
         // Rounds of kRoundBlocks blocks each.
+        const TileStore dst_g(out, tile, nblocks, 1024);
 #pragma unroll
         for (int h = 0; h < kTileBlocks / kRoundBlocks; ++h) {
             if (p / kRoundBlocks == h) {
@@ -583,9 +604,9 @@ __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 
             const uint4 *src = lds + lane;
 #pragma unroll
             for (int u = 0; u < kRoundBlocks; ++u) {
-                const int64_t blk = tile + kRoundBlocks * h + u;
+                const int b = kRoundBlocks * h + u;
                 const uint4 v = src[65 * u];
-                if (blk < nblocks) store_nt(o + blk * 64 + lane, v);
+                if (tile + b < nblocks) dst_g.b128(16 * (64 * b + lane), v);
             }
             wave_lds_sync();
         }
@@ -714,9 +735,10 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     quantize_groups<false>(R, s, t, mw, C);
     store_codes(L, nblocks, lds, codes, C);
     if (L.valid) {
-        micro[L.b * 8 + L.q] = (unsigned short)(mw & 0xFFFFu);  // groups 2q, 2q + 1
-        micro[L.b * 8 + 4 + L.q] = (unsigned short)(mw >> 16);  // groups 2q + 8, 2q + 9
-        if (L.q == 0) block[L.b] = s;
+        const TileStore m(micro, L.tile, nblocks, 16);
+        m.b16(16 * L.p + 2 * L.q, (unsigned short)(mw & 0xFFFFu));      // groups 2q, 2q + 1
+        m.b16(16 * L.p + 8 + 2 * L.q, (unsigned short)(mw >> 16));      // groups 2q + 8, 2q + 9
+        if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, as_u(s));
     }
 }
 
@@ -816,7 +838,8 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
     store_codes(L, nblocks, lds, codes, C);
     if (L.valid && (q & 1) == 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) scales[L.b * 8 + (q >> 1) + 2 * k] = (uint8_t)(e[k] + 127);
+        for (int k = 0; k < 4; ++k)
+            TileStore(scales, L.tile, nblocks, 8).b8(8 * L.p + (q >> 1) + 2 * k, (unsigned char)(e[k] + 127));
     }
 }
 
