@@ -241,18 +241,22 @@ def test_mx_full_size(fp4q):
 
 
 def test_graph_capture_replay(fp4q):
-    """The entry points allocate nothing and never synchronise, so a compress +
-    decompress + reduce sequence can be captured in a HIP graph; every replay
-    (with eager work in between) must equal the eager result."""
+    """The entry points allocate nothing and never synchronise, so every one of
+    them can be captured in a HIP graph; every replay (with eager work in
+    between) must equal the eager result."""
     xb = inputs.make_config("act2048", rows=256)
     x = to_dev(xb)
     codes, micro, block = fp4q.fp4q_compress(x)
     out = fp4q.fp4q_decompress(codes, micro, block)
     peers = [fp4q.fp4q_compress(to_dev(inputs.make_normal(256, 4096, seed=500 + p))) for p in range(3)]
     acc = fp4q.fp4q_decompress_accumulate(peers)
+    req = fp4q.fp4q_reduce_requantize(peers, local=x)
+    mx = fp4q.fp4q_compress_mx(x)
+    mout = fp4q.fp4q_decompress_mx(*mx)
     torch.cuda.synchronize()
-    want = [t.clone() for t in (codes, micro, block, out, acc)]
-    for t in (codes, micro, block, out, acc):
+    bufs = (codes, micro, block, out, acc, *req, *mx, mout)
+    want = [t.clone() for t in bufs]
+    for t in bufs:
         t.zero_()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -263,14 +267,17 @@ def test_graph_capture_replay(fp4q):
             fp4q.fp4q_compress(x, codes, micro, block)
             fp4q.fp4q_decompress(codes, micro, block, out=out)
             fp4q.fp4q_decompress_accumulate(peers, out=acc)
+            fp4q.fp4q_reduce_requantize(peers, *req, local=x)
+            fp4q.fp4q_compress_mx(x, *mx)
+            fp4q.fp4q_decompress_mx(*mx, out=mout)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(4):
-        for t in (codes, micro, block, out, acc):
+        for t in bufs:
             t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip((codes, micro, block, out, acc), want):
+        for a, b in zip(bufs, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d differs" % rep
 
 
