@@ -446,3 +446,40 @@ def test_two_exchange_allreduce_emulated(fp4q):
     rel = np.linalg.norm(o - exact) / np.linalg.norm(exact)
     _say("  emulated 8-rank compressed AllReduce: relative error %.4f" % rel)
     assert rel < 0.25
+
+
+def test_nonfinite_input_stays_in_its_block(fp4q):
+    """Non-finite input is outside the method's domain (the result is unspecified),
+    but every call completes, and blocks without a NaN or an infinity come out
+    exactly as the oracle computes them: the damage stays inside its block."""
+    rows, L = 16, 1024
+    xb = inputs.make_normal(rows, L, seed=950)
+    bad = np.zeros(rows * L // 256, bool)
+    flat = xb.reshape(-1)
+    for blk, val in ((1, 0x7FC0), (6, 0x7F80), (11, 0xFF80), (20, 0x7FC0), (63, 0xFF80)):
+        flat[256 * blk + 37] = val          # bf16 NaN, +Inf, -Inf
+        bad[blk] = True
+    good = np.repeat(~bad, 256).reshape(rows, L)
+    x = to_dev(xb)
+    c, m, b = fp4q.fp4q_compress(x)
+    out = fp4q.fp4q_decompress(c, m, b)
+    acc = fp4q.fp4q_decompress_accumulate([(c, m, b), (c, m, b)])
+    req = fp4q.fp4q_reduce_requantize([(c, m, b)], local=x)
+    mc, ms = fp4q.fp4q_compress_mx(x)
+    mout = fp4q.fp4q_decompress_mx(mc, ms)
+    torch.cuda.synchronize()
+    ref = oracle.compress(xb)
+    g = good.reshape(-1, 256)[:, 0]
+    np.testing.assert_array_equal(c.cpu().numpy().reshape(-1, 128)[g], ref["codes"].reshape(-1, 128)[g])
+    np.testing.assert_array_equal(m.cpu().numpy().reshape(-1, 16)[g], ref["micro"].reshape(-1, 16)[g])
+    np.testing.assert_array_equal(b.cpu().numpy().reshape(-1)[g].view(np.uint32),
+                                  ref["block"].reshape(-1)[g].view(np.uint32))
+    want = oracle.decompress(ref["codes"], ref["micro"], ref["block"])
+    np.testing.assert_array_equal(out.cpu().numpy()[good].view(np.uint32), want[good].view(np.uint32))
+    np.testing.assert_array_equal(acc.cpu().numpy()[good], 2 * want[good])
+    rq = oracle.requantize([(ref["codes"], ref["micro"], ref["block"])], local=xb)
+    np.testing.assert_array_equal(req[0].cpu().numpy().reshape(-1, 128)[g], rq["codes"].reshape(-1, 128)[g])
+    rmx = oracle.compress_mx(xb)
+    np.testing.assert_array_equal(mc.cpu().numpy().reshape(-1, 128)[g], rmx["codes"].reshape(-1, 128)[g])
+    wmx = oracle.decompress_mx(rmx["codes"], rmx["scales"])
+    np.testing.assert_array_equal(mout.cpu().numpy()[good].view(np.uint32), wmx[good].view(np.uint32))
