@@ -124,19 +124,22 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 // Global stores.  Every kernel writes through buffer stores with the
-// system-scope cache policy (sc1): on this GPU they wrote streaming output about
+// system-scope cache policy (sc1): on MI355X they wrote streaming output about
 // 20 % faster than non-temporal global stores (6.1 against 4.9 TB/s on the
 // decompress traffic pattern, 6.95 against 6.5 on the compress pattern).  A
-// wavefront's descriptor covers exactly its tile's part of one output array
-// (the bytes of its valid blocks, so a store past the last block would also be
-// dropped by the hardware range check; the kernels do not issue any).
+// wavefront's descriptor covers exactly its tile's part of one output array:
+// the bytes of its valid blocks, none for a wavefront whose tile lies past the
+// last block (the last workgroup of a launch can hold such wavefronts), so a
+// store past the end would also be dropped by the hardware range check; the
+// kernels issue none.
 constexpr int kStorePolicy = 16;  // sc1
 struct TileStore {
     __amdgpu_buffer_rsrc_t r;
     // bytes_per_block of the array, for the tile's blocks [tile, tile + 16) that exist
     __device__ __forceinline__ TileStore(void *base, int64_t tile, int64_t nblocks,
                                          int bytes_per_block) {
-        const int64_t nvalid = nblocks - tile < kTileBlocks ? nblocks - tile : kTileBlocks;
+        const int64_t left = nblocks - tile;
+        const int64_t nvalid = left < 0 ? 0 : left < kTileBlocks ? left : kTileBlocks;
         r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(base) + tile * bytes_per_block, 0,
                                               static_cast<int>(nvalid * bytes_per_block), 0x00020000);
     }
@@ -273,11 +276,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------- compress
 // Input staging: the wavefront's tile (16 blocks of bf16, 8 KiB, contiguous)
 // is read with eight fully coalesced 1 KiB loads into the wave-private LDS
-// region, then each lane reads its 128 contiguous bytes: register j = element 64 q + j, i.e. register bits 0-5 =
-// index bits 0-5 and lane bits 4, 5 = index bits 6, 7.  After the transform's
-// two exchanges register 16 k + i holds element 16 q + 64 k + i: quarter q owns
-// micro-groups q, q + 4, q + 8, q + 12 (without the transform the same
-// exchanges are made, without butterflies).
+// region, then each lane reads its 128 contiguous bytes: register j = element
+// 64 q + j, i.e. register bits 0-5 = index bits 0-5 and lane bits 4, 5 = index
+// bits 6, 7.  After the transform's two exchanges register 16 k + i holds
+// element 16 q + 64 k + i: quarter q owns micro-groups q, q + 4, q + 8, q + 12
+// (without the transform the same exchanges are made, without butterflies).
 template <bool kFwht>
 __device__ __forceinline__ void compress_transform(float (&R)[64]) {
     if constexpr (kFwht) {
@@ -763,29 +766,9 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
     __shared__ uint4 lds_all[kSenderWaves * kStageChunks];
     const Lane L = lane_map<kSenderWaves>(nblocks);
     uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
-    const int lane = L.lane, p = L.p, q = L.q;
-    {
-        uint4 d[8];
-        load_tile(in, L.tile, nblocks, lane, d);
-        uint4 *dst = lds + 33 * (lane >> 5) + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[66 * j] = d[j];
-    }
-    wave_lds_sync();
+    const int q = L.q;
     float R[64];
-    {
-        const uint4 *srcl = lds + 33 * p + 8 * q;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 x = srcl[i];
-            const unsigned w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                R[8 * i + 2 * k] = as_f(w[k] << 16);
-                R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
-            }
-        }
-    }
+    load_widen(L, in, nblocks, lds, R);
     compress_transform<kFwht>(R);
 
     // exponent of each 32-group; the registers hold 16 y when transformed
