@@ -265,7 +265,8 @@ __device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
 // base plus a constant.
 constexpr int kStageChunks = 528;  // 16 x 33 chunks = 8.25 KiB per wavefront
 // receiver: bf16 output needs 16 x 33 chunks, fp32 output kRoundBlocks x 65
-constexpr int kReceiverChunks = 65 * kRoundBlocks > 528 ? 65 * kRoundBlocks : 528;
+template <bool kBf16>
+constexpr int kReceiverChunks = kBf16 ? 528 : 65 * kRoundBlocks;
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -620,12 +621,12 @@ template <bool kFwht, bool kBf16>
 __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     const uint4 *__restrict__ codes, const uint4 *__restrict__ micro,
     const float *__restrict__ block, int64_t nblocks, void *__restrict__ out) {
-    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
+    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<kBf16>];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
     dequant<kSet>(load_payload(L, codes, micro, block), R);
     receiver_transform<kFwht, kBf16>(R);
-    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
+    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
 }
 
 // --------------------------------------------------- receiver-side reduce
@@ -637,9 +638,11 @@ struct Peers {
 
 // Sum of k payloads into R (mode kFma or kAdd) with kInFlight payloads' loads
 // outstanding: the loads of peer p + kInFlight are issued as soon as peer p has
-// been dequantised.  k is wave-uniform, so every branch here is uniform.
+// been dequantised.  k is wave-uniform, so every branch here is uniform.  One
+// payload in flight measured best: every further buffer costs 12 registers, and
+// the resident wavefronts those registers would allow hide more latency.
 #ifndef FP4Q_PEERS_IN_FLIGHT
-#define FP4Q_PEERS_IN_FLIGHT 4
+#define FP4Q_PEERS_IN_FLIGHT 1
 #endif
 constexpr int kInFlight = FP4Q_PEERS_IN_FLIGHT;
 
@@ -667,14 +670,14 @@ __device__ __forceinline__ void sum_peers(const Lane &L, const Peers &peers, int
 template <bool kFwht, bool kBf16>
 __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
     Peers peers, int k, int64_t nblocks, void *__restrict__ out) {
-    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
+    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<kBf16>];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
     sum_peers<kFma>(L, peers, k, R);
     receiver_transform<kFwht, kBf16>(R);
-    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
+    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
 }
 
 
@@ -832,7 +835,7 @@ template <bool kFwht, bool kBf16>
 __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
     const uint4 *__restrict__ codes, const uint2 *__restrict__ scales, int64_t nblocks,
     void *__restrict__ out) {
-    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks];
+    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<kBf16>];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     const uint4 *src = codes + L.bl * 8 + L.q;
     const uint4 c0 = load_nt(src), c1 = load_nt(src + 4);
@@ -861,7 +864,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
         }
     }
     receiver_transform<kFwht, kBf16>(R);
-    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks, out, R);
+    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
 }
 
 // ------------------------------------------------------------------- host
