@@ -89,9 +89,13 @@ def fp4q_payload_bytes(rows: int, row_len: int):
     return c.value, m.value, b.value
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The HIP stream to launch on: the given torch stream, else the current
+    stream of the tensors' device (a stream belongs to one device)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if s.device != device:
+        raise ValueError("fp4q: stream is on %s, tensors on %s" % (s.device, device))
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -139,11 +143,12 @@ def _arg(t, name, numel, dtypes):
 
 
 def _on_gpu(*tensors):
-    """Every tensor argument in device memory, all on the same GPU."""
+    """Every tensor argument in device memory, all on the same GPU; returns it."""
     dev = tensors[0].device
     for t in tensors:
         if t.device.type != "cuda" or t.device != dev:
             raise ValueError("fp4q: every tensor must be on the same GPU (%s, %s)" % (dev, t.device))
+    return dev
 
 
 def _payload_args(codes, micro, block, n, who):
@@ -167,9 +172,9 @@ def fp4q_compress(x, codes=None, micro_scales=None, block_scales=None, flags: in
         micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
     if block_scales is None:
         block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
-    _on_gpu(x, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
+    gpu = _on_gpu(x, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
     _check(lib().fp4q_compress_ex(_ptr(x), rows, L, _ptr(codes), _ptr(micro_scales),
-                                  _ptr(block_scales), flags, _stream(stream)))
+                                  _ptr(block_scales), flags, _stream(stream, gpu)))
     return codes, micro_scales, block_scales
 
 
@@ -191,9 +196,10 @@ def fp4q_decompress(codes, micro_scales, block_scales, out=None, out_dtype=None,
     pay = _payload_args(codes, micro_scales, block_scales, rows * L, "payload")
     if out is None:
         out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
-    _on_gpu(*pay, _arg(out, "output", rows * L, ("float32", "bfloat16")))
+    gpu = _on_gpu(*pay, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     _check(lib().fp4q_decompress_ex(_ptr(codes), _ptr(micro_scales), _ptr(block_scales), rows, L,
-                                    _ptr(out), _out_dtype_code(out.dtype), flags, _stream(stream)))
+                                    _ptr(out), _out_dtype_code(out.dtype), flags,
+                                    _stream(stream, gpu)))
     return out
 
 
@@ -211,7 +217,7 @@ def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 
         ins += _payload_args(c, m, b, rows * L, "peer %d" % i)
     if out is None:
         out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=dev)
-    _on_gpu(*ins, _arg(out, "output", rows * L, ("float32", "bfloat16")))
+    gpu = _on_gpu(*ins, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     PA = ctypes.c_void_p * max(k, 1)
     cs = PA(*[p[0].data_ptr() for p in payloads])
     ms = PA(*[p[1].data_ptr() for p in payloads])
@@ -219,7 +225,7 @@ def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 
     cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
     _check(lib().fp4q_decompress_accumulate_ex(k, cast(cs), cast(ms), cast(bs), rows, L,
                                                _ptr(out), _out_dtype_code(out.dtype), flags,
-                                               _stream(stream)))
+                                               _stream(stream, gpu)))
     return out
 
 
@@ -250,7 +256,7 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
         micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
     if block_scales is None:
         block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
-    _on_gpu(*ins, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
+    gpu = _on_gpu(*ins, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
     PA = ctypes.c_void_p * max(k, 1)
     cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
     cs = PA(*[p[0].data_ptr() for p in payloads])
@@ -258,7 +264,7 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
     bs = PA(*[p[2].data_ptr() for p in payloads])
     _check(lib().fp4q_reduce_requantize_ex(
         k, cast(cs), cast(ms), cast(bs), _ptr(local) if local is not None else None, rows, L,
-        _ptr(codes), _ptr(micro_scales), _ptr(block_scales), flags, _stream(stream)))
+        _ptr(codes), _ptr(micro_scales), _ptr(block_scales), flags, _stream(stream, gpu)))
     return codes, micro_scales, block_scales
 
 
@@ -271,10 +277,10 @@ def fp4q_compress_mx(x, codes=None, scales=None, flags: int = 0, stream=None):
         codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, L // 32), dtype=torch.uint8, device=x.device)
-    _on_gpu(x, _arg(codes, "output codes", rows * L // 2, ("uint8",)),
+    gpu = _on_gpu(x, _arg(codes, "output codes", rows * L // 2, ("uint8",)),
             _arg(scales, "output scales", rows * L // 32, ("uint8",)))
     _check(lib().fp4q_compress_mx(_ptr(x), rows, L, _ptr(codes), _ptr(scales), flags,
-                                  _stream(stream)))
+                                  _stream(stream, gpu)))
     return codes, scales
 
 
@@ -287,7 +293,7 @@ def fp4q_decompress_mx(codes, scales, out=None, out_dtype=None, flags: int = 0, 
     _arg(scales, "scales", rows * L // 32, ("uint8",))
     if out is None:
         out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
-    _on_gpu(codes, scales, _arg(out, "output", rows * L, ("float32", "bfloat16")))
+    gpu = _on_gpu(codes, scales, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     _check(lib().fp4q_decompress_mx(_ptr(codes), _ptr(scales), rows, L, _ptr(out),
-                                    _out_dtype_code(out.dtype), flags, _stream(stream)))
+                                    _out_dtype_code(out.dtype), flags, _stream(stream, gpu)))
     return out
