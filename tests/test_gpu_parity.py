@@ -483,3 +483,22 @@ def test_nonfinite_input_stays_in_its_block(fp4q):
     np.testing.assert_array_equal(mc.cpu().numpy().reshape(-1, 128)[g], rmx["codes"].reshape(-1, 128)[g])
     wmx = oracle.decompress_mx(rmx["codes"], rmx["scales"])
     np.testing.assert_array_equal(mout.cpu().numpy()[good].view(np.uint32), wmx[good].view(np.uint32))
+
+
+@pytest.mark.parametrize("fwht", [True, False])
+def test_full_size_invariances(fp4q, fwht):
+    """On the 32768 x 4096 tensor, on the GPU alone: negating the input leaves
+    every scale and every code magnitude unchanged, and scaling it by 2^-7
+    leaves codes and micro-scales unchanged and scales each block scale by
+    exactly 2^-7 (both follow from the method's definition)."""
+    flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+    x = to_dev(inputs.make_config("large32768")).view(torch.bfloat16)
+    c, m, b = fp4q.fp4q_compress(x, flags=flags)
+    cn, mn, bn = fp4q.fp4q_compress(-x, flags=flags)
+    cs, ms, bs = fp4q.fp4q_compress(x * 2.0 ** -7, flags=flags)    # exact in bf16 here
+    torch.cuda.synchronize()
+    assert torch.equal(b.view(torch.int32), bn.view(torch.int32))
+    assert torch.equal(m, mn)
+    assert torch.equal(c & 0x77, cn & 0x77)                        # magnitudes of both nibbles
+    assert torch.equal(c, cs) and torch.equal(m, ms)
+    assert torch.equal(b * 2.0 ** -7, bs)
