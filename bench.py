@@ -270,6 +270,50 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
     return res
 
 
+def variant_timing(fp4q, torch, X, P, Y, iters: int = 40):
+    """The other entry points on the same 32768 x 4096 buffers (three rotating
+    sets, HIP events around every launch, a queued head start): median launch
+    time, algorithmic bytes and the HBM roofline fraction."""
+    n = X[0].numel()
+    S = len(X)
+    nf = fp4q.FP4Q_FLAG_NO_FWHT
+    Yb = [torch.empty(X[0].shape, dtype=torch.bfloat16, device=X[0].device) for _ in range(S)]
+    MX = [fp4q.fp4q_compress_mx(X[s]) for s in range(S)]
+    pay = n // 2 + n // 16 + n // 64
+    mx_pay = n // 2 + n // 32
+    cases = (
+        ("decompress_bf16_out", lambda s: fp4q.fp4q_decompress(*P[s], out=Yb[s]), pay + 2 * n),
+        ("compress_no_fwht", lambda s: fp4q.fp4q_compress(X[s], *P[s], flags=nf), 2 * n + pay),
+        ("decompress_no_fwht", lambda s: fp4q.fp4q_decompress(*P[s], out=Y[s], flags=nf), pay + 4 * n),
+        ("compress_mx", lambda s: fp4q.fp4q_compress_mx(X[s], *MX[s]), 2 * n + mx_pay),
+        ("decompress_mx", lambda s: fp4q.fp4q_decompress_mx(*MX[s], out=Y[s]), mx_pay + 4 * n),
+    )
+    res = {}
+    for name, fn, nbytes in cases:
+        for i in range(6):
+            fn(i % S)
+        torch.cuda.synchronize()
+        for i in range(16):
+            fn(i % S)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            fn(i % S)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        med = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+        gbps = nbytes / med / 1e9
+        res[name] = {"median_us": round(med * 1e6, 2), "algorithmic_bytes": nbytes,
+                     "achieved_GBps": round(gbps, 1), "frac": round(gbps / PEAK_GBPS, 4)}
+        log("variant %-20s median %7.1f us  %7.1f GB/s  %.1f%% of HBM peak" % (
+            name, med * 1e6, gbps, 100 * gbps / PEAK_GBPS))
+    # restore the payloads the step uses (the no-transform compress overwrote them)
+    for s in range(S):
+        fp4q.fp4q_compress(X[s], *P[s])
+    torch.cuda.synchronize()
+    return res
+
+
 def fwht_tradeoff(fp4q, inputs, torch, dev, iters: int = 50):
     """Throughput and relative RMSE with and without the transform on the activation
     (2048x4096) and outlier (8192x4096) workloads.  These tensors fit in the 256 MB
@@ -551,6 +595,7 @@ def main():
                                         (t_c.mean() + t_d.mean()) / 1e9 / PEAK_GBPS, 4),
         "rel_rmse": {"fwht": round(rmse, 6), "no_fwht": round(rmse_nf, 6)},
     }
+    result["variants"] = variant_timing(fp4q, torch, X, P, Y)
     if not args.no_receiver:
         result["receiver"] = receiver_timing(fp4q, inputs, torch, dev)
     if not args.no_tradeoff:

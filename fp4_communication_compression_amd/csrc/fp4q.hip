@@ -249,11 +249,13 @@ __device__ __forceinline__ void transpose4(T &x0, T &x1, T &x2, T &x3) {
     swap32(x1, x3);
 }
 
+// Two fp32 values rounded to nearest-even bf16, lo in the low half: one
+// v_cvt_pk_bf16_f32 (denormals kept, as the whole library is built).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
-    unsigned a = as_u(lo), b = as_u(hi);
-    a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
-    b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
-    return a | b;
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
 // Wave-private LDS staging: a wavefront exchanges data among its own lanes
@@ -264,9 +266,10 @@ __device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
 // access patterns are free of bank conflicts and every address is a per-lane
 // base plus a constant.
 constexpr int kStageChunks = 528;  // 16 x 33 chunks = 8.25 KiB per wavefront
-// receiver: bf16 output needs 16 x 33 chunks, fp32 output kRoundBlocks x 65
+// receiver output staging: bf16 all 16 blocks of 33 chunks at once, fp32 in
+// rounds of kRoundBlocks blocks of 65 chunks
 template <bool kBf16>
-constexpr int kReceiverChunks = kBf16 ? 528 : 65 * kRoundBlocks;
+constexpr int kReceiverChunks = kBf16 ? 16 * 33 : 65 * kRoundBlocks;
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
