@@ -506,7 +506,7 @@ __device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *
 // sum (kAdd, the order the re-quantisation defines).
 enum DequantMode { kSet, kFma, kAdd };
 template <DequantMode kMode>
-__device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64]) {
+__device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64], float dscale = 1.0f) {
     const unsigned C[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
     const float S[4] = {P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 0),
                         P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 1),
@@ -516,7 +516,7 @@ __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64]) {
     for (int w = 0; w < 8; ++w) {
         const float Sg = S[w >> 1];
         static_for<4>([&](auto sel) {
-            const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], 1.0f, decltype(sel)::value);
+            const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], dscale, decltype(sel)::value);
             const int j = 8 * w + 2 * decltype(sel)::value;
             if constexpr (kMode == kFma) {
                 R[j] = fmaf(f[0], Sg, R[j]);
@@ -542,7 +542,7 @@ __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64]) {
 //   bf16 out: with index bits 3, 4 -> register j holds (j & 7) + 8 q + 32 (j >> 3).
 // Without the transform only the exchanges are made.
 template <bool kFwht, bool kBf16>
-__device__ __forceinline__ void receiver_transform(float (&R)[64]) {
+__device__ __forceinline__ void receiver_transform(float (&R)[64], bool scaled = false) {
     constexpr int kA = kBf16 ? 8 : 4;    // register bit that takes index bit 5
     constexpr int kB = kBf16 ? 16 : 8;   // register bit that takes index bit 6
     if constexpr (kFwht) {
@@ -558,9 +558,24 @@ __device__ __forceinline__ void receiver_transform(float (&R)[64]) {
     if constexpr (kFwht) {
         stage<kB>(R);  // index bit 6
         stage<32>(R);  // index bit 7
+        if (!scaled) {  // wave-uniform
 #pragma unroll
-        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+            for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+        }
     }
+}
+
+// The transform's 1/16 may be applied by the FP4 decode instead (its scale
+// operand is a power of two), which saves the 64 multiplies at the end: every
+// value and partial sum is then exactly 1/16 of what the unscaled order
+// computes, as long as none of them is subnormal.  Nonzero partial sums are
+// multiples of the smallest unit in the last place among the block's decoded
+// values, which is at least s * 2^-34 for block scale s (E2M1 >= 0.5, E4M3 >=
+// 2^-9, 24-bit significands); so s >= 2^-80 on every lane of the wavefront
+// keeps them all above 2^-114 and the result bit-identical.  The vote is
+// wave-uniform, so both paths stay free of divergence.
+__device__ __forceinline__ bool fold_sixteenth(float block_scale) {
+    return __builtin_amdgcn_ballot_w64(block_scale >= 0x1p-80f) == ~0ull;
 }
 
 // Output staging: every lane's values go through the wave-private LDS region so
@@ -627,8 +642,10 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<kBf16>];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
-    dequant<kSet>(load_payload(L, codes, micro, block), R);
-    receiver_transform<kFwht, kBf16>(R);
+    const PayloadRegs P = load_payload(L, codes, micro, block);
+    const bool fold = kFwht && fold_sixteenth(P.s);
+    dequant<kSet>(P, R, fold ? 0.0625f : 1.0f);
+    receiver_transform<kFwht, kBf16>(R, fold);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
 }
 
@@ -846,10 +863,15 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
     const int e0 = (int)((sw.x >> (8 * L.q)) & 0xFFu) - 127;  // group q
     const int e1 = (int)((sw.y >> (8 * L.q)) & 0xFFu) - 127;  // group q + 4
     const unsigned C[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    // the transform's 1/16 goes into the decode scale when every group's
+    // exponent is at least -100: decoded values are multiples of 2^(e - 1), so
+    // no value or partial sum comes near the subnormal range (see
+    // fold_sixteenth); the vote is wave-uniform
+    const bool fold = kFwht && __builtin_amdgcn_ballot_w64(e0 >= -100 && e1 >= -100) == ~0ull;
     float R[64];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int e = h ? e1 : e0;
+        const int e = (h ? e1 : e0) - (fold ? 4 : 0);
         // 2^e as the conversion's scale; 2^-127 is subnormal, so use 2^-126 and halve
         const float sc = as_f((unsigned)((e < -126 ? -126 : e) + 127) << 23);
 #pragma unroll
@@ -866,7 +888,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
             for (int j = 32 * h; j < 32 * h + 32; ++j) R[j] *= 0.5f;  // exact
         }
     }
-    receiver_transform<kFwht, kBf16>(R);
+    receiver_transform<kFwht, kBf16>(R, fold);
     store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
 }
 
