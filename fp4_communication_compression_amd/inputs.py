@@ -162,3 +162,37 @@ def make_edge_case(kind: str, rows: int, row_len: int, seed: int = 0) -> np.ndar
     else:
         raise ValueError(kind)
     return f32_to_bf16_bits(v).reshape(rows, row_len)
+
+
+def make_random_mixture(rows: int, row_len: int, seed: int) -> np.ndarray:
+    """Random stress input (bf16 bits): every row has its own scale 2^u, u uniform
+    in [-30, 30], and every 256-block its own kind -- normal, Student-t (nu=2),
+    uniform, sparse normal (75 % zeros), constant, one spike among small
+    values, bf16-subnormal tiny values, or small integers (rounding ties)."""
+    rng = np.random.default_rng(seed)
+    nb = row_len // 256
+    v = np.empty((rows, nb, 256), np.float64)
+    kinds = rng.integers(0, 8, size=(rows, nb))
+    for r in range(rows):
+        scale = 2.0 ** rng.uniform(-30, 30)
+        for b in range(nb):
+            k = kinds[r, b]
+            if k == 0:
+                blk = rng.standard_normal(256)
+            elif k == 1:
+                blk = rng.standard_t(2, 256)
+            elif k == 2:
+                blk = rng.uniform(-1, 1, 256)
+            elif k == 3:
+                blk = rng.standard_normal(256) * (rng.random(256) < 0.25)
+            elif k == 4:
+                blk = np.full(256, rng.standard_normal())
+            elif k == 5:
+                blk = rng.standard_normal(256) * 1e-3
+                blk[rng.integers(256)] = 100.0
+            elif k == 6:
+                blk = rng.standard_normal(256) * 2.0 ** -128 / scale
+            else:
+                blk = rng.integers(-6, 7, 256).astype(np.float64) / scale
+            v[r, b] = blk * scale
+    return f32_to_bf16_bits(v.reshape(rows, row_len).astype(np.float32))

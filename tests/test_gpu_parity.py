@@ -502,3 +502,56 @@ def test_full_size_invariances(fp4q, fwht):
     assert torch.equal(c & 0x77, cn & 0x77)                        # magnitudes of both nibbles
     assert torch.equal(c, cs) and torch.equal(m, ms)
     assert torch.equal(b * 2.0 ** -7, bs)
+
+
+@pytest.mark.parametrize("chunk", range(10))
+def test_random_sweep(fp4q, chunk):
+    """Seeded random shapes (1-40 rows, 256-6144 columns) and random per-row
+    scales and per-block kinds (make_random_mixture), 400 cases in all, through
+    every entry point, against the oracle under the parity rule."""
+    rng = np.random.default_rng(4000 + chunk)
+    mismatches = 0
+    for case in range(40):
+        rows, L = int(rng.integers(1, 41)), 256 * int(rng.integers(1, 25))
+        seed = int(rng.integers(1 << 30))
+        fwht = bool(rng.integers(2))
+        flags = 0 if fwht else fp4q.FP4Q_FLAG_NO_FWHT
+        _say("sweep %d.%d: %dx%d seed %d fwht %s" % (chunk, case, rows, L, seed, fwht))
+        xb = inputs.make_random_mixture(rows, L, seed)
+        ref = oracle.compress(xb, fwht=fwht, debug=True)
+        st = parity.check_compress(gpu_compress(fp4q, xb, flags), ref)
+        mismatches += st["code_mismatch"] + st["micro_mismatch"]
+        dp = [to_dev(ref[k]) for k in ("codes", "micro", "block")]
+        out = fp4q.fp4q_decompress(*dp, flags=flags)
+        outb = fp4q.fp4q_decompress(*dp, out_dtype=torch.bfloat16, flags=flags)
+        torch.cuda.synchronize()
+        want = oracle.decompress(ref["codes"], ref["micro"], ref["block"], fwht=fwht)
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        np.testing.assert_array_equal(outb.cpu().view(torch.int16).numpy().view(np.uint16),
+                                      inputs.f32_to_bf16_bits(want))
+        # MX round trip
+        rmx = oracle.compress_mx(xb, fwht=fwht, debug=True)
+        mc, ms = fp4q.fp4q_compress_mx(to_dev(xb), flags=flags)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ms.cpu().numpy(), rmx["scales"])
+        from tests import bruteforce as bfm
+        gc, rc = parity.unpack(mc.cpu().numpy()), parity.unpack(rmx["codes"])
+        assert np.all((gc == rc) | bfm.near(rmx["v"].reshape(-1), bfm.e2m1_boundaries(), 1e-6))
+        mo = fp4q.fp4q_decompress_mx(to_dev(rmx["codes"]), to_dev(rmx["scales"]), flags=flags)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(
+            mo.cpu().numpy().view(np.uint32),
+            oracle.decompress_mx(rmx["codes"], rmx["scales"], fwht=fwht).view(np.uint32))
+        if case % 4 == 0:   # receivers: k peers (plus a local slice for the re-quantisation)
+            k = int(rng.integers(1, 17))
+            peers = [inputs.make_random_mixture(rows, L, seed + 1 + p) for p in range(k)]
+            trip = [(r["codes"], r["micro"], r["block"])
+                    for r in (oracle.compress(p, fwht=fwht) for p in peers)]
+            dev_trip = [tuple(to_dev(a) for a in t) for t in trip]
+            acc = fp4q.fp4q_decompress_accumulate(dev_trip, flags=flags)
+            req = fp4q.fp4q_reduce_requantize(dev_trip, local=to_dev(xb), flags=flags)
+            torch.cuda.synchronize()
+            parity.check_rowwise(acc.cpu().numpy(), oracle.accumulate_f64(trip, fwht=fwht))
+            parity.check_compress([o.cpu().numpy() for o in req],
+                                  oracle.requantize(trip, debug=True, local=xb, fwht=fwht))
+    _say("  sweep chunk %d: %d tolerated near-boundary mismatches" % (chunk, mismatches))
