@@ -45,13 +45,15 @@ def check_compress(gpu, ref, rel: float = 1e-6) -> dict:
             "elements": int(gc.size)}
 
 
-def check_rowwise(gpu: np.ndarray, ref: np.ndarray, rel: float = 1e-6) -> float:
+def check_rowwise(gpu: np.ndarray, ref: np.ndarray, rel: float = 1e-6, magnitude=None) -> float:
     """Per row: max |gpu - ref| <= rel * max |ref|; a zero row must be exactly zero.
-    Returns the largest row ratio."""
+    With ``magnitude`` (per element, e.g. the sum of the peers' |terms| of a
+    reduce), the row scale is max magnitude instead: the accuracy any fp32
+    summation can reach when the terms cancel.  Returns the largest row ratio."""
     g = np.asarray(gpu, np.float64).reshape(ref.shape[0], -1)
     r = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
     err = np.abs(g - r).max(axis=1)
-    scale = np.abs(r).max(axis=1)
+    scale = np.abs(r if magnitude is None else np.asarray(magnitude, np.float64).reshape(r.shape)).max(axis=1)
     assert np.all(err <= rel * scale), "row error above %g of the row maximum" % rel
     with np.errstate(invalid="ignore", divide="ignore"):
         ratio = np.where(scale > 0, err / scale, 0.0)
