@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 from fp4_communication_compression_amd import inputs
+from tests import bruteforce as bfm
 from tests import parity
 
 pytestmark = pytest.mark.gpu
@@ -214,7 +215,6 @@ def run_mx(fp4q, xb, fwht, name):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sc.cpu().numpy(), ref["scales"])
     gc, rc = parity.unpack(c.cpu().numpy()), parity.unpack(ref["codes"])
-    from tests import bruteforce as bfm
     near = bfm.near(ref["v"].reshape(-1), bfm.e2m1_boundaries(), 1e-6)
     assert np.all((gc == rc) | near)
     assert np.count_nonzero(gc != rc) == 0
@@ -539,7 +539,6 @@ def test_random_sweep(fp4q, chunk):
         mc, ms = fp4q.fp4q_compress_mx(to_dev(xb), flags=flags)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(ms.cpu().numpy(), rmx["scales"])
-        from tests import bruteforce as bfm
         gc, rc = parity.unpack(mc.cpu().numpy()), parity.unpack(rmx["codes"])
         assert np.all((gc == rc) | bfm.near(rmx["v"].reshape(-1), bfm.e2m1_boundaries(), 1e-6))
         mo = fp4q.fp4q_decompress_mx(to_dev(rmx["codes"]), to_dev(rmx["scales"]), flags=flags)
