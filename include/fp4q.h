@@ -107,7 +107,9 @@ int fp4q_decompress_ex(const uint8_t *codes, const uint8_t *micro_scales,
  * when the call returns).  1 <= k <= FP4Q_MAX_PEERS.  `out` is overwritten with
  * the sum, fp32 or bf16 (out_dtype).  The sum is taken in fp32 in the transform
  * domain (one inverse transform for all peers), so it matches an exact sum to
- * about 1e-7 of the row's largest value, not bit for bit. */
+ * about 1e-7 of the row's largest summed magnitude (sum over p of |term p|),
+ * not bit for bit; that equals 1e-7 of the row's largest result unless the
+ * peers' terms cancel. */
 int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,
                                const uint8_t *const *micro_scales,
                                const float *const *block_scales, int64_t rows,
