@@ -456,6 +456,40 @@ def copy_reference(torch, dev):
     del src, dst
 
 
+def copy_ceiling(torch, dev, nbytes: int = 512 << 20, iters: int = 20):
+    """A plain device-to-device copy (the runtime's copy kernel) between two
+    buffers of nbytes, timed with HIP events: the GB/s (bytes read + written)
+    a copy reaches on this GPU, as context for the roofline fractions."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(3)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def copy(i):
+        src, dst = bufs[i % 3], bufs[(i + 1) % 3]
+        rc = hip.hipMemcpyAsync(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                nbytes, 3, stream)  # 3 = device to device
+        if rc != 0:
+            raise RuntimeError("hipMemcpyAsync failed: %d" % rc)
+    for i in range(4):
+        copy(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        copy(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    med = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    del bufs
+    gbps = 2 * nbytes / med / 1e9
+    log("copy ceiling: %d MiB device copy %.1f us, %.0f GB/s (read + write)" % (nbytes >> 20, med * 1e6, gbps))
+    return {"bytes_per_copy": nbytes, "median_us": round(med * 1e6, 1), "GBps_read_plus_write": round(gbps, 1),
+            "frac": round(gbps / PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -596,6 +630,7 @@ def main():
         "rel_rmse": {"fwht": round(rmse, 6), "no_fwht": round(rmse_nf, 6)},
     }
     result["variants"] = variant_timing(fp4q, torch, X, P, Y)
+    result["copy_ceiling"] = copy_ceiling(torch, dev)
     if not args.no_receiver:
         result["receiver"] = receiver_timing(fp4q, inputs, torch, dev)
     if not args.no_tradeoff:
