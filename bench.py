@@ -492,11 +492,12 @@ def copy_ceiling(torch, dev, nbytes: int = 512 << 20, iters: int = 20):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--gpus", type=int, default=1, help="number of GPUs (only 1 is supported)")
+    ap.add_argument("--steps", type=int, default=400, help="timed compress + decompress steps")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before them")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--sets", type=int, default=3,
+                    help="rotating buffer sets (keeps reads out of the last-level cache)")
     ap.add_argument("--no-receiver", action="store_true",
                     help="skip the receiver-kernel timings on the k=8 reduce workload")
     ap.add_argument("--receiver-only", action="store_true",
@@ -519,9 +520,9 @@ def main():
         print(summarize_trace(args.summarize_trace))
         return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the method shards by block range "
-              "with no halo; the multi-GPU exchange is not part of it); run with --gpus 1",
-              file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU; the library has no multi-GPU exchange "
+              "(the method shards by block range with no halo, so a GPU's share is measured "
+              "as is); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
