@@ -18,19 +18,22 @@
 //
 // Transform: radix-2 stages in the order stride 1, 2, ..., 128 (index bit 0 to
 // 7).  A stage on a register bit is a butterfly between two registers.  An index
-// bit that sits in a lane bit is first exchanged with an already transformed
-// register bit by v_permlane16_swap (lane bit 4) or v_permlane32_swap (lane bit
-// 5), one instruction per register pair, and then transformed in registers.
-// The order of these exchanges is chosen per kernel so that
+// bit that sits in a lane bit is first brought into the registers, in exchange
+// for an already transformed register bit, and then transformed in registers.
+// The receivers exchange with v_permlane16_swap (lane bit 4) or
+// v_permlane32_swap (lane bit 5), one instruction per register pair; compress,
+// whose time is VALU issue (a lane swap costs the issue slots of two adds),
+// makes its one exchange (index bits 4-5 for 6-7) through LDS instead.  The
+// order of the exchanges is chosen per kernel so that
 //   * the receiver's payload loads of the four quarters cover whole 64-byte
 //     segments per instruction (non-temporal path),
 //   * compress ends with four whole micro-groups per lane, so group maxima,
 //     scales, quantisation and packing stay in registers,
 //   * the receiver ends with 16-byte register quads of contiguous output.
-// LDS only re-deals data between that lane-local layout and fully coalesced
-// 1 KiB-per-instruction global accesses (the bf16 input tile, the codes and the
-// output), in a region private to each wavefront.  No MFMA: the work is
-// streaming and the transform is butterflies.
+// Otherwise LDS only re-deals data between that lane-local layout and fully
+// coalesced 1 KiB-per-instruction global accesses (the bf16 input tile, the
+// codes and the output), in a region private to each wavefront.  No MFMA: the
+// work is streaming and the transform is butterflies.
 //
 // Numerics follow the method's fp32 operation order exactly (built with
 // -ffp-contract=off, IEEE division, fp32 denormals kept):
@@ -280,13 +283,57 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------- compress
 // Input staging: the wavefront's tile (16 blocks of bf16, 8 KiB, contiguous)
 // is read with eight fully coalesced 1 KiB loads into the wave-private LDS
-// region, then each lane reads its 128 contiguous bytes: register j = element
-// 64 q + j, i.e. register bits 0-5 = index bits 0-5 and lane bits 4, 5 = index
-// bits 6, 7.  After the transform's two exchanges register 16 k + i holds
-// element 16 q + 64 k + i: quarter q owns micro-groups q, q + 4, q + 8, q + 12
-// (without the transform the same exchanges are made, without butterflies).
+// region, then each lane reads 128 bytes of its block.  The layout compress
+// quantises from is register 16 k + i = element 16 q + 64 k + i: quarter q owns
+// micro-groups q, q + 4, q + 8, q + 12 (index bits 0-3 and 6-7 in the register
+// index, bits 4-5 in lane bits 4-5).  Without the transform the lane reads that
+// layout straight from LDS.  With it, the first six stages need index bits 0-5
+// in registers: the lane reads register j = element 64 q + j, transforms, and
+// trades index bits 4-5 for 6-7 through LDS before the last two stages (the
+// LDS pipe is idle there, while lane swaps would cost VALU issue slots, which
+// bound this kernel).
+
+// Index bits 4-5 (register bits 4-5) change places with index bits 6-7 (lane
+// bits 4-5) through the wavefront's LDS region, in two rounds by register bit 3,
+// which stays put: round r writes the lane's registers whose bit 3 is r as eight
+// 16-byte chunks and reads eight back.  Chunk (h, a, b) holds the four elements
+// 4 h + 8 r + 16 a + 64 b .. + 3 of block p, at chunk 33 p + h + 2 a + 8 b.
+// Before: register j = element 64 q + j.  After: register 16 k + i = element
+// 16 q + 64 k + i.  The caller has finished any earlier use of the region.
+__device__ __forceinline__ void exchange_through_lds(const Lane &L, uint4 *__restrict__ lds,
+                                                     float (&R)[64]) {
+    uint4 *wr = lds + 33 * L.p + 8 * L.q;        // b = q
+    const uint4 *rd = lds + 33 * L.p + 2 * L.q;  // a = q
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        wave_lds_sync();
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j = 16 * a + 8 * r + 4 * h;
+                wr[h + 2 * a] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 x = rd[h + 8 * b];
+                const int j = 16 * b + 8 * r + 4 * h;
+                R[j] = as_f(x.x);
+                R[j + 1] = as_f(x.y);
+                R[j + 2] = as_f(x.z);
+                R[j + 3] = as_f(x.w);
+            }
+    }
+}
+
+// The transform from the input layout (register j = element 64 q + j) to the
+// quantisation layout; without the transform the input already has that layout.
 template <bool kFwht>
-__device__ __forceinline__ void compress_transform(float (&R)[64]) {
+__device__ __forceinline__ void compress_transform(const Lane &L, uint4 *__restrict__ lds,
+                                                   float (&R)[64]) {
     if constexpr (kFwht) {
         stage<1>(R);   // level 1: index bits 0-3
         stage<2>(R);
@@ -294,11 +341,10 @@ __device__ __forceinline__ void compress_transform(float (&R)[64]) {
         stage<8>(R);
         stage<16>(R);  // level 2: index bits 4-7
         stage<32>(R);
+        exchange_through_lds(L, lds, R);
+        stage<16>(R);  // index bit 6, now register bit 4
+        stage<32>(R);  // index bit 7, now register bit 5
     }
-    swap_lane4<16>(R);  // register bit 4 <-> lane bit 4: index bit 6 in, 4 out
-    if constexpr (kFwht) stage<16>(R);
-    swap_lane5<32>(R);  // register bit 5 <-> lane bit 5: index bit 7 in, 5 out
-    if constexpr (kFwht) stage<32>(R);
 }
 
 // Scales and codes of the four register groups of a lane (registers
@@ -363,15 +409,26 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
     }
 }
 
-// Codes of a tile through LDS (8 chunks per block, stride 9): C[0..3] is the
-// lane's 16-byte chunk q of its block, C[4..7] chunk q + 4; the tile's 2 KiB of
-// codes then leave in two 1 KiB stores.  The caller has finished any earlier use
-// of the LDS region.
+// Codes of a tile through LDS (8 chunks per block, stride 9); the tile's 2 KiB
+// of codes then leave in two 1 KiB stores.  The caller has finished any earlier
+// use of the LDS region.  Where the lane's eight code dwords go:
+//   kGroups = false: C[0..3] is the 16-byte chunk q of its block, C[4..7] chunk q + 4;
+//   kGroups = true (the compress layout, dword w = registers 8 w .. 8 w + 7 =
+//     elements 16 q + 64 (w >> 1) + 8 (w & 1) ..): C[w] is dword
+//     2 q + 8 (w >> 1) + (w & 1) of the block, so C[2 m], C[2 m + 1] is one
+//     8-byte write (chunk (q >> 1) + 2 m, dwords 2 (q & 1), + 1).
+template <bool kGroups>
 __device__ __forceinline__ void store_codes(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
                                             uint4 *__restrict__ codes, const unsigned (&C)[8]) {
     const int lane = L.lane;
-    lds[9 * L.p + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
-    lds[9 * L.p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
+    if constexpr (kGroups) {
+        uint2 *dst = reinterpret_cast<uint2 *>(lds + 9 * L.p + (L.q >> 1)) + (L.q & 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[4 * m] = make_uint2(C[2 * m], C[2 * m + 1]);
+    } else {
+        lds[9 * L.p + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
+        lds[9 * L.p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
+    }
     wave_lds_sync();
     const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
     const TileStore out(codes, L.tile, nblocks, 128);
@@ -403,8 +460,11 @@ __device__ __forceinline__ void load_tile(const uint4 *__restrict__ in, int64_t 
 }
 
 // The wavefront's bf16 tile staged through its LDS region (kStageChunks
-// chunks); each lane then reads its 128 contiguous bytes and widens them:
-// register j = element 64 q + j of block p (exact).
+// chunks); each lane then reads 128 bytes of its block p and widens them
+// (exactly):
+//   kGroups = false: register j = element 64 q + j (the lane's 128 contiguous bytes);
+//   kGroups = true:  register 16 k + i = element 16 q + 64 k + i (four runs of 32 bytes).
+template <bool kGroups>
 __device__ __forceinline__ void load_widen(const Lane &L, const uint4 *__restrict__ in,
                                            int64_t nblocks, uint4 *__restrict__ lds,
                                            float (&R)[64]) {
@@ -416,14 +476,16 @@ __device__ __forceinline__ void load_widen(const Lane &L, const uint4 *__restric
         for (int j = 0; j < 8; ++j) dst[66 * j] = d[j];
     }
     wave_lds_sync();
-    const uint4 *srcl = lds + 33 * L.p + 8 * L.q;
+    const uint4 *srcl = lds + 33 * L.p + (kGroups ? 2 : 8) * L.q;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint4 x = srcl[i];
+        // registers 8 i .. 8 i + 7 come from chunk i, or (grouped) chunk
+        // 2 q + 8 (i >> 1) + (i & 1) of the block
+        const uint4 x = srcl[kGroups ? 8 * (i >> 1) + (i & 1) : i];
         const unsigned w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            R[8 * i + 2 * k] = as_f(w[k] << 16);              // bf16 -> fp32, exact
+            R[8 * i + 2 * k] = as_f(w[k] << 16);
             R[8 * i + 2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
         }
     }
@@ -438,32 +500,20 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
 
     float R[64];
-    load_widen(L, in, nblocks, lds, R);
-    compress_transform<kFwht>(R);
+    load_widen<!kFwht>(L, in, nblocks, lds, R);
+    compress_transform<kFwht>(L, lds, R);
 
     float s, t[4];
     unsigned mw, C[8];
     quantize_groups<kFwht>(R, s, t, mw, C);
 
-    // Code dword w of quarter q holds elements 8 e .. 8 e + 7 with index bits
-    // (3, 6, 7) = bits of w and (4, 5) = bits of q.  Re-deal the dwords so that q
-    // holds index bits 5, 6 and w bits (3, 4, 7): 16-byte chunk q (dwords 0-3)
-    // and chunk q + 4 (dwords 4-7) of the block's 128 code bytes.
-    swap32(C[0], C[2]);  // lane bit 5 (index bit 5) <-> dword bit 1 (index bit 6)
-    swap32(C[1], C[3]);
-    swap32(C[4], C[6]);
-    swap32(C[5], C[7]);
-    swap16(C[0], C[2]);  // lane bit 4 (index bit 4) <-> dword bit 1 (index bit 5)
-    swap16(C[1], C[3]);
-    swap16(C[4], C[6]);
-    swap16(C[5], C[7]);
     // micro-scales: quarter q holds groups q + 4k; make it groups 4q .. 4q + 3
     transpose4(t[0], t[1], t[2], t[3]);
     mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
     mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
 
-    wave_lds_sync();  // every lane has read its input chunks
-    store_codes(L, nblocks, lds, codes, C);
+    wave_lds_sync();  // every lane has read its chunks from the region
+    store_codes<true>(L, nblocks, lds, codes, C);
     if (L.valid) {
         TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, mw);
         if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, as_u(s));
@@ -747,7 +797,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     uint4 *lds = lds_all + (threadIdx.x / kWave) * kChunks;
     float R[64];
     if constexpr (kLocal) {
-        load_widen(L, local, nblocks, lds, R);
+        load_widen<false>(L, local, nblocks, lds, R);
         local_transform<kFwht>(R);
         wave_lds_sync();  // every lane has read its input chunks
     } else {
@@ -759,7 +809,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     float s, t[4];
     unsigned mw, C[8];
     quantize_groups<false>(R, s, t, mw, C);
-    store_codes(L, nblocks, lds, codes, C);
+    store_codes<false>(L, nblocks, lds, codes, C);
     if (L.valid) {
         const TileStore m(micro, L.tile, nblocks, 16);
         m.b16(16 * L.p + 2 * L.q, (unsigned short)(mw & 0xFFFFu));      // groups 2q, 2q + 1
@@ -791,8 +841,8 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
     uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
     const int q = L.q;
     float R[64];
-    load_widen(L, in, nblocks, lds, R);
-    compress_transform<kFwht>(R);
+    load_widen<!kFwht>(L, in, nblocks, lds, R);
+    compress_transform<kFwht>(L, lds, R);
 
     // exponent of each 32-group; the registers hold 16 y when transformed
     int e[4];
@@ -831,17 +881,8 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
         });
         C[w] = c;
     }
-    // same re-dealing of code dwords as compress
-    swap32(C[0], C[2]);
-    swap32(C[1], C[3]);
-    swap32(C[4], C[6]);
-    swap32(C[5], C[7]);
-    swap16(C[0], C[2]);
-    swap16(C[1], C[3]);
-    swap16(C[4], C[6]);
-    swap16(C[5], C[7]);
-    wave_lds_sync();  // every lane has read its input chunks
-    store_codes(L, nblocks, lds, codes, C);
+    wave_lds_sync();  // every lane has read its chunks from the region
+    store_codes<true>(L, nblocks, lds, codes, C);
     if (L.valid && (q & 1) == 0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
