@@ -293,34 +293,40 @@ __device__ __forceinline__ void wave_lds_sync() {
 // LDS pipe is idle there, while lane swaps would cost VALU issue slots, which
 // bound this kernel).
 
-// Index bits 4-5 (register bits 4-5) change places with index bits 6-7 (lane
-// bits 4-5) through the wavefront's LDS region, in two rounds by register bit 3,
-// which stays put: round r writes the lane's registers whose bit 3 is r as eight
-// 16-byte chunks and reads eight back.  Chunk (h, a, b) holds the four elements
-// 4 h + 8 r + 16 a + 64 b .. + 3 of block p, at chunk 33 p + h + 2 a + 8 b.
-// Before: register j = element 64 q + j.  After: register 16 k + i = element
-// 16 q + 64 k + i.  The caller has finished any earlier use of the region.
+// Two index bits held in lane bits 4-5 (call their value B) change places with
+// the two index bits held in register bits kMoved, kMoved + 1 (value A), through
+// the wavefront's LDS region (at least 528 chunks), in two rounds by register
+// bit kRound, which stays put like register bits 0-2: round r writes the lane's
+// 32 registers whose bit kRound is r as eight 16-byte chunks and reads eight
+// back.  The chunk holding register bit 2 = c, A = a, B = b of block p sits at
+// chunk 33 p + c + 2 a + 8 b: written by lane (p, q = b) from its registers with
+// A = a, read by lane (p, q = a) into its registers with A = b.  The caller has
+// finished any earlier use of the region.
+template <int kMoved, int kRound>
 __device__ __forceinline__ void exchange_through_lds(const Lane &L, uint4 *__restrict__ lds,
                                                      float (&R)[64]) {
-    uint4 *wr = lds + 33 * L.p + 8 * L.q;        // b = q
-    const uint4 *rd = lds + 33 * L.p + 2 * L.q;  // a = q
+    static_assert(kMoved >= 3 && kMoved + 1 <= 5 && kRound >= 3 && kRound <= 5 &&
+                      kRound != kMoved && kRound != kMoved + 1,
+                  "register bits 0-2 stay; kMoved, kMoved + 1 and kRound are the other three");
+    uint4 *wr = lds + 33 * L.p + 8 * L.q;
+    const uint4 *rd = lds + 33 * L.p + 2 * L.q;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         wave_lds_sync();
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int j = 16 * a + 8 * r + 4 * h;
-                wr[h + 2 * a] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
+            for (int c = 0; c < 2; ++c) {
+                const int j = (a << kMoved) | (r << kRound) | (c << 2);
+                wr[c + 2 * a] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
             }
         wave_lds_sync();
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint4 x = rd[h + 8 * b];
-                const int j = 16 * b + 8 * r + 4 * h;
+            for (int c = 0; c < 2; ++c) {
+                const uint4 x = rd[c + 8 * b];
+                const int j = (b << kMoved) | (r << kRound) | (c << 2);
                 R[j] = as_f(x.x);
                 R[j + 1] = as_f(x.y);
                 R[j + 2] = as_f(x.z);
@@ -341,7 +347,9 @@ __device__ __forceinline__ void compress_transform(const Lane &L, uint4 *__restr
         stage<8>(R);
         stage<16>(R);  // level 2: index bits 4-7
         stage<32>(R);
-        exchange_through_lds(L, lds, R);
+        // index bits 6-7 (lanes) for 4-5 (register bits 4-5): afterwards register
+        // 16 k + i = element 16 q + 64 k + i
+        exchange_through_lds<4, 3>(L, lds, R);
         stage<16>(R);  // index bit 6, now register bit 4
         stage<32>(R);  // index bit 7, now register bit 5
     }
@@ -399,7 +407,9 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const float r = inv[w >> 1];
-        unsigned c = 0;
+        // the four conversions write all four bytes of c; starting from a
+        // register that dies here (instead of 0) saves a move per dword
+        unsigned c = as_u(R[8 * w]);
         static_for<4>([&](auto sel) {
             const int j = 8 * w + 2 * decltype(sel)::value;
             c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j] * r, R[j + 1] * r, 1.0f,
@@ -588,13 +598,17 @@ __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64], fl
 // chosen so that the output's 16-byte stores cover whole 64-byte segments:
 //   fp32 out: with index bits 2, 3 -> register j of quarter q holds element
 //     (j & 3) + 4 q + 32 (j >> 2 & 1) + 64 (j >> 3 & 1) + 16 (j >> 4 & 1)
-//     + 128 (j >> 5);
-//   bf16 out: with index bits 3, 4 -> register j holds (j & 7) + 8 q + 32 (j >> 3).
-// Without the transform only the exchanges are made.
+//     + 128 (j >> 5), by lane swaps one bit at a time;
+//   bf16 out: with index bits 3, 4 -> register j holds (j & 7) + 8 q + 32 (j >> 3),
+//     through LDS, both bits at once: the region is free until the output
+//     staging, and the exchange takes 64 lane swaps (128 VALU issue slots) off
+//     the VALU (the fp32 receiver's region is sized for its output rounds, and
+//     its stores bound it).
+// Without the transform only the exchanges are made.  lds: the wavefront's
+// region (kReceiverChunks<kBf16> chunks), free on entry; in use on return.
 template <bool kFwht, bool kBf16>
-__device__ __forceinline__ void receiver_transform(float (&R)[64], bool scaled = false) {
-    constexpr int kA = kBf16 ? 8 : 4;    // register bit that takes index bit 5
-    constexpr int kB = kBf16 ? 16 : 8;   // register bit that takes index bit 6
+__device__ __forceinline__ void receiver_transform(const Lane &L, uint4 *__restrict__ lds,
+                                                   float (&R)[64], bool scaled = false) {
     if constexpr (kFwht) {
         stage<1>(R);   // index bits 0-4
         stage<2>(R);
@@ -602,11 +616,20 @@ __device__ __forceinline__ void receiver_transform(float (&R)[64], bool scaled =
         stage<8>(R);
         stage<16>(R);
     }
-    swap_lane4<kA>(R);
-    if constexpr (kFwht) stage<kA>(R);   // index bit 5
-    swap_lane5<kB>(R);
+    if constexpr (kBf16) {
+        exchange_through_lds<3, 5>(L, lds, R);
+        wave_lds_sync();  // the region's reads are done before the output staging
+        if constexpr (kFwht) {
+            stage<8>(R);   // index bit 5
+            stage<16>(R);  // index bit 6
+        }
+    } else {
+        swap_lane4<4>(R);
+        if constexpr (kFwht) stage<4>(R);  // index bit 5
+        swap_lane5<8>(R);
+        if constexpr (kFwht) stage<8>(R);  // index bit 6
+    }
     if constexpr (kFwht) {
-        stage<kB>(R);  // index bit 6
         stage<32>(R);  // index bit 7
         if (!scaled) {  // wave-uniform
 #pragma unroll
@@ -695,8 +718,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     const PayloadRegs P = load_payload(L, codes, micro, block);
     const bool fold = kFwht && fold_sixteenth(P.s);
     dequant<kSet>(P, R, fold ? 0.0625f : 1.0f);
-    receiver_transform<kFwht, kBf16>(R, fold);
-    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
+    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
+    receiver_transform<kFwht, kBf16>(L, wl, R, fold);
+    store_out<kBf16>(L, nblocks, wl, out, R);
 }
 
 // --------------------------------------------------- receiver-side reduce
@@ -746,8 +770,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
     sum_peers<kFma>(L, peers, k, R);
-    receiver_transform<kFwht, kBf16>(R);
-    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
+    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
+    receiver_transform<kFwht, kBf16>(L, wl, R);
+    store_out<kBf16>(L, nblocks, wl, out, R);
 }
 
 
@@ -874,7 +899,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const float sc = scale[w >> 1];
-        unsigned c = 0;
+        unsigned c = as_u(R[8 * w]);  // every byte is written below (as in compress)
         static_for<4>([&](auto sel) {
             const int j = 8 * w + 2 * decltype(sel)::value;
             c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j], R[j + 1], sc, decltype(sel)::value);
@@ -929,8 +954,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
             for (int j = 32 * h; j < 32 * h + 32; ++j) R[j] *= 0.5f;  // exact
         }
     }
-    receiver_transform<kFwht, kBf16>(R, fold);
-    store_out<kBf16>(L, nblocks, lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>, out, R);
+    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
+    receiver_transform<kFwht, kBf16>(L, wl, R, fold);
+    store_out<kBf16>(L, nblocks, wl, out, R);
 }
 
 // ------------------------------------------------------------------- host
