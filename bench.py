@@ -631,7 +631,10 @@ def main():
         "rel_rmse": {"fwht": round(rmse, 6), "no_fwht": round(rmse_nf, 6)},
     }
     result["variants"] = variant_timing(fp4q, torch, X, P, Y)
-    result["copy_ceiling"] = copy_ceiling(torch, dev)
+    # the copy ceiling's 512 MiB copies would join the counter-scale reference's
+    # 256 MiB copies in a --copy-reference run (the summary takes the largest copies)
+    if not args.copy_reference:
+        result["copy_ceiling"] = copy_ceiling(torch, dev)
     if not args.no_receiver:
         result["receiver"] = receiver_timing(fp4q, inputs, torch, dev)
     if not args.no_tradeoff:
