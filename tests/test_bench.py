@@ -1,0 +1,122 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic byte counts the
+roofline uses, the single-GPU guard, and the rocprofv3 summaries that the
+committed profiles and the bench line's `traffic` come from."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+N_LARGE = 32768 * 4096
+
+
+def test_algorithmic_bytes():
+    # per element: compress 2 (bf16 in) + 0.5 (codes) + 1/16 (micro) + 4/256 (block);
+    # decompress the payload in and 4 (fp32) out
+    ab = bench.algorithmic_bytes(N_LARGE)
+    assert ab["compress"] == 346030080 == int(N_LARGE * 2.578125)
+    assert ab["decompress"] == 614465536 == int(N_LARGE * 4.578125)
+
+
+def test_receiver_bytes():
+    rb = bench._receiver_bytes()
+    n = 4096 * 11008
+    payload = 26066944                          # codes + micro + block of one peer
+    assert n // 2 + n // 16 + n // 64 == payload
+    assert rb["accumulate"] == 388890624 == 8 * payload + 4 * n
+    assert rb["requantize"] == 9 * payload      # 8 payloads in, 1 out
+    assert rb["requantize_local"] == 7 * payload + 2 * n + payload
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+COUNTER_FIELDS = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _counter_dir(tmp_path, name, counter, rows):
+    d = tmp_path / name / "host"
+    d.mkdir(parents=True)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, COUNTER_FIELDS)
+        w.writeheader()
+        for i, (kernel, grid, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Grid_Size": grid, "Kernel_Name": kernel,
+                        "Counter_Name": counter, "Counter_Value": value})
+    return str(tmp_path / name)
+
+
+COPY = "__amd_rocclr_copyBuffer"
+COMP = "void (anonymous namespace)::compress_kernel<true>(uint4 const*, long, uint4*, unsigned int*, float*)"
+DECOMP = "void (anonymous namespace)::decompress_kernel<true, false>(uint4 const*, uint4 const*, float const*, long, void*)"
+G = N_LARGE // 64          # one thread per 64 elements
+KIB = bench.COPY_REF_BYTES // 1024
+
+
+def test_counter_summary_scales_by_the_copy_reference(tmp_path):
+    # a counter that reads half of what a copy reads (fetch) and one that reads all of it (write)
+    ab = bench.algorithmic_bytes(N_LARGE)
+    fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE", [
+        (COPY, 131072, KIB / 2), (COPY, 131072, KIB / 2 + 3), (COPY, 131072, KIB / 2 - 3),
+        (COPY, 512, 2),                                         # a tiny copy: another grid, ignored
+        (COMP, G, 2 * N_LARGE / 1024 / 2), (COMP, G // 4, 1.0),  # a smaller launch: ignored
+        (DECOMP, G, (ab["decompress"] - 4 * N_LARGE) / 2048),
+    ])
+    write = _counter_dir(tmp_path, "w", "WRITE_SIZE", [
+        (COPY, 131072, KIB), (COPY, 131072, KIB), (COPY, 131072, KIB),
+        (COMP, G, (ab["compress"] - 2 * N_LARGE) / 1024), (DECOMP, G, 4 * N_LARGE / 1024),
+    ])
+    text = bench.summarize_counters(fetch, write)
+    assert "fetch x2.000, write x1.000" in text
+    traffic = dict(kv.split("=") for kv in text.splitlines()[-1].split()[1:])
+    assert traffic.pop("source") == bench.kernel_source_hash()
+    assert int(traffic["compress"]) == ab["compress"]
+    assert int(traffic["decompress"]) == ab["decompress"]
+    assert "| compress | 32768x4096 |" in text and "| 1.000 |" in text
+
+
+def test_counter_summary_refuses_copies_of_two_sizes(tmp_path):
+    # a 512 MiB copy has the same grid as the 256 MiB reference (grid-strided copy
+    # kernel): a run holding both cannot give the scale
+    fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE", [
+        (COPY, 131072, KIB / 2), (COPY, 131072, KIB), (COMP, G, 1.0)])
+    write = _counter_dir(tmp_path, "w", "WRITE_SIZE", [
+        (COPY, 131072, KIB), (COPY, 131072, 2 * KIB), (COMP, G, 1.0)])
+    with pytest.raises(ValueError, match="more than one size"):
+        bench.summarize_counters(fetch, write)
+
+
+def test_trace_summary(tmp_path):
+    d = tmp_path / "t" / "host"
+    d.mkdir(parents=True)
+    fields = ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp", "End_Timestamp"]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fields)
+        w.writeheader()
+        t = 0
+        for grid, us in [(G, 100), (G, 110), (G, 120), (G // 8, 5)]:   # ns timestamps
+            w.writerow({"Kernel_Name": DECOMP, "Grid_Size_X": grid, "Grid_Size_Y": 1, "Grid_Size_Z": 1,
+                        "Start_Timestamp": t, "End_Timestamp": t + us * 1000})
+            t += 10 ** 6
+        w.writerow({"Kernel_Name": "some_other_kernel", "Grid_Size_X": 64, "Grid_Size_Y": 1,
+                    "Grid_Size_Z": 1, "Start_Timestamp": 0, "End_Timestamp": 5})
+    text = bench.summarize_trace(str(tmp_path / "t"))
+    rows = [l for l in text.splitlines() if l.startswith("| decompress_kernel")]
+    assert rows == ["| decompress_kernel<true, false> | %d | 3 | 110.00 | 110.00 | 100.00 | 120.00 |" % G]
+    assert "some_other_kernel" not in text
+
+
+def test_traffic_is_read_only_for_the_current_kernel_source(tmp_path, monkeypatch):
+    f = tmp_path / "summary.md"
+    f.write_text("text\ntraffic: source=%s compress=11 decompress=22\n" % bench.kernel_source_hash())
+    assert bench.measured_traffic(str(f)) == {"compress": 11, "decompress": 22}
+    f.write_text("text\ntraffic: source=0123456789abcdef compress=11 decompress=22\n")
+    assert bench.measured_traffic(str(f)) is None
+    assert bench.measured_traffic(str(tmp_path / "missing.md")) is None
