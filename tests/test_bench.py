@@ -82,15 +82,20 @@ def test_counter_summary_scales_by_the_copy_reference(tmp_path):
     assert "| compress | 32768x4096 |" in text and "| 1.000 |" in text
 
 
-def test_counter_summary_refuses_copies_of_two_sizes(tmp_path):
-    # a 512 MiB copy has the same grid as the 256 MiB reference (grid-strided copy
-    # kernel): a run holding both cannot give the scale
+def test_counter_summary_reference_is_the_largest_copies(tmp_path):
+    # smaller copies (tensor clones) share the grid-strided copy kernel's grid and
+    # are left out; the reference needs its three copies
     fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE", [
-        (COPY, 131072, KIB / 2), (COPY, 131072, KIB), (COMP, G, 1.0)])
+        (COPY, 131072, KIB / 2), (COPY, 131072, KIB / 2), (COPY, 131072, KIB / 2),
+        (COPY, 131072, KIB / 16), (COPY, 131072, KIB / 200), (COMP, G, 1.0)])
     write = _counter_dir(tmp_path, "w", "WRITE_SIZE", [
-        (COPY, 131072, KIB), (COPY, 131072, 2 * KIB), (COMP, G, 1.0)])
-    with pytest.raises(ValueError, match="more than one size"):
-        bench.summarize_counters(fetch, write)
+        (COPY, 131072, KIB), (COPY, 131072, KIB), (COPY, 131072, KIB),
+        (COPY, 131072, KIB / 8), (COMP, G, 1.0)])
+    assert "fetch x2.000, write x1.000" in bench.summarize_counters(fetch, write)
+    no_ref = _counter_dir(tmp_path, "w2", "WRITE_SIZE", [
+        (COPY, 131072, KIB / 8), (COMP, G, 1.0)])
+    with pytest.raises(ValueError, match="three reference copies"):
+        bench.summarize_counters(fetch, no_ref)
 
 
 def test_trace_summary(tmp_path):
