@@ -99,6 +99,17 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """An output tensor allocated for the stream the kernel will run on, so that
+    torch's caching allocator does not hand its memory to other work while that
+    stream may still be writing it."""
+    import torch
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -167,11 +178,11 @@ def fp4q_compress(x, codes=None, micro_scales=None, block_scales=None, flags: in
     _arg(x, "input", rows * L, _BF16_BITS)
     dev = x.device
     if codes is None:
-        codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
+        codes = _empty((rows, L // 2), torch.uint8, dev, stream)
     if micro_scales is None:
-        micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
+        micro_scales = _empty((rows, L // 16), torch.uint8, dev, stream)
     if block_scales is None:
-        block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
+        block_scales = _empty((rows, L // 256), torch.float32, dev, stream)
     gpu = _on_gpu(x, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
     _check(lib().fp4q_compress_ex(_ptr(x), rows, L, _ptr(codes), _ptr(micro_scales),
                                   _ptr(block_scales), flags, _stream(stream, gpu)))
@@ -195,7 +206,7 @@ def fp4q_decompress(codes, micro_scales, block_scales, out=None, out_dtype=None,
     L = 2 * half
     pay = _payload_args(codes, micro_scales, block_scales, rows * L, "payload")
     if out is None:
-        out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
+        out = _empty((rows, L), out_dtype or torch.float32, codes.device, stream)
     gpu = _on_gpu(*pay, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     _check(lib().fp4q_decompress_ex(_ptr(codes), _ptr(micro_scales), _ptr(block_scales), rows, L,
                                     _ptr(out), _out_dtype_code(out.dtype), flags,
@@ -216,7 +227,7 @@ def fp4q_decompress_accumulate(payloads, out=None, out_dtype=None, flags: int = 
     for i, (c, m, b) in enumerate(payloads):
         ins += _payload_args(c, m, b, rows * L, "peer %d" % i)
     if out is None:
-        out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=dev)
+        out = _empty((rows, L), out_dtype or torch.float32, dev, stream)
     gpu = _on_gpu(*ins, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     PA = ctypes.c_void_p * max(k, 1)
     cs = PA(*[p[0].data_ptr() for p in payloads])
@@ -251,11 +262,11 @@ def fp4q_reduce_requantize(payloads, codes=None, micro_scales=None, block_scales
     if local is not None:
         ins.append(_arg(local, "local slice", rows * L, _BF16_BITS))
     if codes is None:
-        codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=dev)
+        codes = _empty((rows, L // 2), torch.uint8, dev, stream)
     if micro_scales is None:
-        micro_scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=dev)
+        micro_scales = _empty((rows, L // 16), torch.uint8, dev, stream)
     if block_scales is None:
-        block_scales = torch.empty((rows, L // 256), dtype=torch.float32, device=dev)
+        block_scales = _empty((rows, L // 256), torch.float32, dev, stream)
     gpu = _on_gpu(*ins, *_payload_args(codes, micro_scales, block_scales, rows * L, "output"))
     PA = ctypes.c_void_p * max(k, 1)
     cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
@@ -274,9 +285,9 @@ def fp4q_compress_mx(x, codes=None, scales=None, flags: int = 0, stream=None):
     rows, L = _dims(x)
     _arg(x, "input", rows * L, _BF16_BITS)
     if codes is None:
-        codes = torch.empty((rows, L // 2), dtype=torch.uint8, device=x.device)
+        codes = _empty((rows, L // 2), torch.uint8, x.device, stream)
     if scales is None:
-        scales = torch.empty((rows, L // 32), dtype=torch.uint8, device=x.device)
+        scales = _empty((rows, L // 32), torch.uint8, x.device, stream)
     gpu = _on_gpu(x, _arg(codes, "output codes", rows * L // 2, ("uint8",)),
             _arg(scales, "output scales", rows * L // 32, ("uint8",)))
     _check(lib().fp4q_compress_mx(_ptr(x), rows, L, _ptr(codes), _ptr(scales), flags,
@@ -292,7 +303,7 @@ def fp4q_decompress_mx(codes, scales, out=None, out_dtype=None, flags: int = 0, 
     _arg(codes, "codes", rows * L // 2, ("uint8",))
     _arg(scales, "scales", rows * L // 32, ("uint8",))
     if out is None:
-        out = torch.empty((rows, L), dtype=out_dtype or torch.float32, device=codes.device)
+        out = _empty((rows, L), out_dtype or torch.float32, codes.device, stream)
     gpu = _on_gpu(codes, scales, _arg(out, "output", rows * L, ("float32", "bfloat16")))
     _check(lib().fp4q_decompress_mx(_ptr(codes), _ptr(scales), rows, L, _ptr(out),
                                     _out_dtype_code(out.dtype), flags, _stream(stream, gpu)))

@@ -302,6 +302,19 @@ def test_concurrent_streams(fp4q):
             for a, b in zip(res[i][0], ref[i]):
                 assert torch.equal(a, b)
             assert torch.equal(res[i][1], ref_out[i])
+    # the same with the stream passed explicitly (outputs allocated for it)
+    for _ in range(3):
+        for i, s in enumerate(streams):
+            s.wait_stream(torch.cuda.current_stream())
+            p = fp4q.fp4q_compress(xs[i], stream=s)
+            res[i] = (p, fp4q.fp4q_decompress(*p, stream=s))
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a, b in zip(res[i][0], ref[i]):
+                assert torch.equal(a, b)
+            assert torch.equal(res[i][1], ref_out[i])
 
 
 def test_offsets_beyond_32_bits(fp4q):
