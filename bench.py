@@ -160,12 +160,16 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> str:
     return "\n".join(out)
 
 
-def summarize_trace(trace_dir: str) -> str:
+def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
     """Per-dispatch kernel durations from a rocprofv3 --kernel-trace run (markdown):
-    each of this library's kernel instantiations at its largest grid."""
+    each of this library's kernel instantiations at its largest grid.  With
+    timed_steps K (the run's --steps), also the headline kernels' launches of the
+    timed region alone: the K launches before the last one (the last
+    compress / decompress pair at full size is the error report's)."""
     rows = []
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))   # dispatch order
     groups = {}
     for r in rows:
         m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel(?:<[^>]*>)?)",
@@ -176,11 +180,20 @@ def summarize_trace(trace_dir: str) -> str:
         groups.setdefault(m.group(1), []).append((grid, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     out = ["| kernel | grid (threads) | calls | average us | median us | min us | max us |",
            "|---|---|---|---|---|---|---|"]
+    timed = []
     for name in sorted(groups, key=lambda n: -len(groups[n])):
         g = max(x[0] for x in groups[name])
         d = np.array([x[1] for x in groups[name] if x[0] == g])
         out.append("| %s | %d | %d | %.2f | %.2f | %.2f | %.2f |" % (
             name, g, len(d), d.mean(), float(np.median(d)), d.min(), d.max()))
+        if timed_steps and name in ("compress_kernel<true>", "decompress_kernel<true, false>") \
+                and len(d) > timed_steps:
+            t = d[-timed_steps - 1:-1]
+            timed.append("| %s | %d | %.2f | %.2f | %.2f |" % (name, len(t), t.mean(),
+                                                              float(np.median(t)), float(np.percentile(t, 90))))
+    if timed:
+        out += ["", "Timed region (%d steps):" % timed_steps, "",
+                "| kernel | calls | average us | median us | p90 us |", "|---|---|---|---|---|"] + timed
     return "\n".join(out)
 
 
@@ -516,6 +529,9 @@ def main():
                     help="also run a plain %d-byte device copy (counter scale reference)" % COPY_REF_BYTES)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--timed-steps", type=int, default=0,
+                    help="with --summarize-trace: the traced run's --steps, to report its timed "
+                         "region's launches of the headline kernels on their own")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the kernel durations of a rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args()
@@ -523,7 +539,7 @@ def main():
         print(summarize_counters(*args.summarize_counters))
         return
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace))
+        print(summarize_trace(args.summarize_trace, args.timed_steps))
         return
     if args.gpus != 1:
         print("bench.py: the benchmark runs on one GPU; the library has no multi-GPU exchange "

@@ -115,7 +115,10 @@ def test_trace_summary(tmp_path):
     text = bench.summarize_trace(str(tmp_path / "t"))
     rows = [l for l in text.splitlines() if l.startswith("| decompress_kernel")]
     assert rows == ["| decompress_kernel<true, false> | %d | 3 | 110.00 | 110.00 | 100.00 | 120.00 |" % G]
-    assert "some_other_kernel" not in text
+    assert "some_other_kernel" not in text and "Timed region" not in text
+    # the timed region of a 2-step run: the two full-size launches before the last one
+    text = bench.summarize_trace(str(tmp_path / "t"), timed_steps=2)
+    assert "| decompress_kernel<true, false> | 2 | 105.00 | 105.00 |" in text
 
 
 def test_traffic_is_read_only_for_the_current_kernel_source(tmp_path, monkeypatch):
