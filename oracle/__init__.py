@@ -37,11 +37,18 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+# A test may point the loader at another build of the oracle (the mutation check
+# of tests/test_oracle_mutations.py loads copies with one planted mistake each).
+LIB_ENV = "FP4Q_ORACLE_LIB"
+
+
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get(LIB_ENV)
+        if not path:
+            path = build()
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         I = ctypes.c_int
