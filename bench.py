@@ -40,6 +40,14 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_large32768.md")
 RECEIVER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_reduce_k8.md")
 COPY_REF_BYTES = 256 << 20
 EVENT_EVERY = 8
+HEADLINE = "large32768"
+#: the step's workloads: what each tensor is (shapes and seeds in inputs.CONFIGS)
+WORKLOADS = {
+    "large32768": "bf16 32768x4096 N(0,1) seed 3",
+    "act2048": "bf16 2048x4096 N(0,1) x exp(N(0,0.5)) per row, seed 1",
+    "outlier8192": "bf16 8192x4096 Student-t(3), 4 fixed columns x100, seed 2",
+}
+ROTATION_BYTES = 512 << 20   # rotating buffer sets span at least twice the last-level cache
 
 
 def log(*a):
@@ -509,14 +517,70 @@ def copy_ceiling(torch, dev, nbytes: int = 512 << 20, iters: int = 20):
             "frac": round(gbps / PEAK_GBPS, 4)}
 
 
+def graph_timed_steps(torch, fp4q, step, X, P, Y, S, args, min_steps: int = 40):
+    """The timed steps as replays of a HIP graph of m steps (m a multiple of the
+    S buffer sets, at least min_steps): on tensors this small, launching from
+    Python would take longer than the kernels.  Per-kernel durations: HIP events
+    around replays of graphs of m compress launches and of m decompress launches
+    on the same rotation, divided by m."""
+    m = S * -(-min_steps // S)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(m):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        return g
+
+    g_step = capture(step)
+    g_c = capture(lambda i: fp4q.fp4q_compress(X[i % S], *P[i % S]))
+    g_d = capture(lambda i: fp4q.fp4q_decompress(*P[(i % S - 1) % S], out=Y[i % S]))
+    torch.cuda.synchronize()
+    log("graph of %d steps; warmup %d" % (m, args.warmup))
+    for _ in range(-(-args.warmup // m)):
+        g_step.replay()
+    torch.cuda.synchronize()
+    reps = -(-args.steps // m)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g_step.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {}
+    for name, g in (("compress", g_c), ("decompress", g_d)):
+        g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(10)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per[name] = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3 / m
+    timing = ("HIP graph replays of %d steps; per-kernel: HIP events around replays of graphs of %d "
+              "launches of each kernel, divided by %d" % (m, m, m))
+    return reps * m, wall, per["compress"], per["decompress"], timing
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1, help="number of GPUs (only 1 is supported)")
     ap.add_argument("--steps", type=int, default=400, help="timed compress + decompress steps")
     ap.add_argument("--warmup", type=int, default=100, help="untimed steps before them")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--sets", type=int, default=3,
-                    help="rotating buffer sets (keeps reads out of the last-level cache)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=HEADLINE,
+                    help="the tensor each step compresses and decompresses (default: the "
+                         "32768x4096 headline workload)")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="time the steps as HIP graph replays (auto: for every workload but the "
+                         "headline, where the eager launches keep ahead of the GPU)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating buffer sets (default: enough to span %d MiB, at least 3, "
+                         "which keeps reads out of the last-level cache)" % (ROTATION_BYTES >> 20))
     ap.add_argument("--no-receiver", action="store_true",
                     help="skip the receiver-kernel timings on the k=8 reduce workload")
     ap.add_argument("--receiver-only", action="store_true",
@@ -558,12 +622,14 @@ def main():
             copy_reference(torch, dev)
         print(json.dumps({"receiver": receiver_timing(fp4q, inputs, torch, dev)}), flush=True)
         return
-    rows, L = 32768, 4096
+    wl = args.workload
+    rows, L = inputs.CONFIGS[wl][:2]
     n = rows * L
-    log("generating large32768 (%dx%d) ..." % (rows, L))
-    xb = inputs.make_config("large32768")
+    log("generating %s (%dx%d) ..." % (wl, rows, L))
+    xb = inputs.make_config(wl)
     x0 = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
-    S = max(2, args.sets)
+    per_set = sum(algorithmic_bytes(n).values()) - (n // 2 + n // 16 + n // 64)  # in + payload + out
+    S = max(2, args.sets) if args.sets else max(3, -(-ROTATION_BYTES // per_set))
     X = [x0] + [x0.clone() for _ in range(S - 1)]
     P = [fp4q.fp4q_compress(X[s]) for s in range(S)]
     Y = [torch.empty((rows, L), dtype=torch.float32, device=dev) for _ in range(S)]
@@ -583,27 +649,33 @@ def main():
     if args.copy_reference:
         copy_reference(torch, dev)
 
-    log("warmup %d" % args.warmup)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    use_graph = args.graph == "on" or (args.graph == "auto" and wl != HEADLINE)
+    if use_graph:
+        K, wall, t_c, t_d, timing = graph_timed_steps(torch, fp4q, step, X, P, Y, S, args)
+    else:
+        log("warmup %d" % args.warmup)
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
 
-    # Per-kernel durations: HIP events on the launch stream around both kernels of
-    # every EVENT_EVERY-th step of the timed region (an event pair costs a few us
-    # of GPU time, so recording them on every step would slow the steps down).
-    K = args.steps
-    sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(args.warmup + i, evs.get(i))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_c = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e-3
-    t_d = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e-3
-    log("timed %d steps: %.3f ms/step; compress %.1f us, decompress %.1f us (mean of %d sampled steps)" %
-        (K, wall / K * 1e3, t_c.mean() * 1e6, t_d.mean() * 1e6, len(sampled)))
+        # Per-kernel durations: HIP events on the launch stream around both kernels of
+        # every EVENT_EVERY-th step of the timed region (an event pair costs a few us
+        # of GPU time, so recording them on every step would slow the steps down).
+        K = args.steps
+        sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
+        evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(args.warmup + i, evs.get(i))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_c = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e-3
+        t_d = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e-3
+        timing = ("eager launches; per-kernel: HIP events around both kernels of every %dth timed "
+                  "step" % EVENT_EVERY)
+    log("timed %d steps: %.3f ms/step; compress %.1f us, decompress %.1f us (mean of %d samples)" %
+        (K, wall / K * 1e3, t_c.mean() * 1e6, t_d.mean() * 1e6, len(t_c)))
 
     ab = algorithmic_bytes(n)
     kern = {}
@@ -626,11 +698,12 @@ def main():
     rmse_nf = float(torch.linalg.vector_norm(out_nf.double() - xf) / torch.linalg.vector_norm(xf))
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if wl == HEADLINE else METRIC.replace("32768x4096", "%dx%d" % (rows, L)),
         "value": round(2 * n * K / wall / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
+        "timing": timing,
         "warmup": args.warmup,
         "ms_per_step": round(wall / K * 1e3, 4),
         "higher_is_better": True,
@@ -638,12 +711,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "large32768: bf16 32768x4096 N(0,1) seed 3; compress + decompress "
-                               "(fp32 out) per step, 3 rotating buffer sets",
+        "config": {"workload": "%s: %s; compress + decompress (fp32 out) per step, %d rotating "
+                               "buffer sets" % (wl, WORKLOADS[wl], S),
                    "rows": rows, "row_len": L, "block": 256, "micro_group": 16},
         "roofline": {"bound": "hbm", "achieved": kern[dom]["achieved_GBps"], "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": kern[dom]["frac"],
-                     "traffic": (measured_traffic() or {}).get(dom),
+                     # the counter summary is the headline workload's
+                     "traffic": (measured_traffic() or {}).get(dom) if wl == HEADLINE else None,
                      "kernel": dom},
         "kernels": kern,
         # the whole step (compress + decompress) against the HBM roofline, by wall clock
