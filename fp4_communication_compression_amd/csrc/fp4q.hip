@@ -20,20 +20,21 @@
 // 7).  A stage on a register bit is a butterfly between two registers.  An index
 // bit that sits in a lane bit is first brought into the registers, in exchange
 // for an already transformed register bit, and then transformed in registers.
-// The receivers exchange with v_permlane16_swap (lane bit 4) or
+// The fp32-output receivers exchange with v_permlane16_swap (lane bit 4) or
 // v_permlane32_swap (lane bit 5), one instruction per register pair; compress,
-// whose time is VALU issue (a lane swap costs the issue slots of two adds),
-// makes its one exchange (index bits 4-5 for 6-7) through LDS instead.  The
+// whose time is VALU issue (a lane swap costs the issue slots of two adds), and
+// the bf16-output receivers make their exchange through LDS instead.  The
 // order of the exchanges is chosen per kernel so that
-//   * the receiver's payload loads of the four quarters cover whole 64-byte
+//   * decompress's payload loads of the four quarters cover whole 64-byte
 //     segments per instruction (non-temporal path),
 //   * compress ends with four whole micro-groups per lane, so group maxima,
 //     scales, quantisation and packing stay in registers,
 //   * the receiver ends with 16-byte register quads of contiguous output.
 // Otherwise LDS only re-deals data between that lane-local layout and fully
 // coalesced 1 KiB-per-instruction global accesses (the bf16 input tile, the
-// codes and the output), in a region private to each wavefront.  No MFMA: the
-// work is streaming and the transform is butterflies.
+// multi-peer kernels' code loads, the codes and the output), in a region
+// private to each wavefront.  No MFMA: the work is streaming and the transform
+// is butterflies.
 //
 // Numerics follow the method's fp32 operation order exactly (built with
 // -ffp-contract=off, IEEE division, fp32 denormals kept):
@@ -80,6 +81,7 @@ constexpr int kSenderWaves = FP4Q_SENDER_WAVES;
 constexpr int kReceiverWaves = FP4Q_RECEIVER_WAVES;
 // fp32 receiver output is staged kRoundBlocks blocks (65 chunks each) at a time
 constexpr int kRoundBlocks = FP4Q_RECEIVER_ROUND;
+
 
 struct Lane {
     int lane;     // 0..63
@@ -531,8 +533,13 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
 }
 
 // --------------------------------------------------- receiver: one payload
-// Loads: instruction h of quarter q reads code chunk q + 4 h (16 bytes = 32
-// codes), so the four quarters read 64 contiguous bytes per instruction.
+// Code layout in the lane: chunks q and q + 4 of its block (16 bytes = 32 codes
+// each).  Decompress loads them so, instruction h of quarter q reading chunk
+// q + 4 h: the four quarters read 64 contiguous bytes per instruction.  The
+// multi-peer kernels instead read each peer's 2 KiB of tile codes as two
+// contiguous 1 KiB loads and re-deal them through LDS (redeal_codes): 3 % faster
+// over 8 peers, but 7 % slower for decompress's single payload, whose one load
+// round then carries the LDS round trip on its critical path.
 // Register j = 32 h + 8 w + t holds element 32 q + 128 h + 8 w + t: register
 // bits 0-4 = index bits 0-4, bit 5 = index bit 7; lane bits 4, 5 = index bits
 // 5, 6.  Its micro-group is (j >> 4 & 1) + 2 q + 8 h, so register group j >> 4
@@ -545,20 +552,47 @@ struct PayloadRegs {
 };
 
 // The block's 16 micro-scale bytes arrive in one 16-byte load (the four lanes of
-// a block read the same 16 bytes); each lane keeps its two byte pairs.
-__device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *__restrict__ codes,
+// a block read the same 16 bytes); each lane keeps its two byte pairs.  kContig:
+// the codes in the contiguous order, for redeal_codes.
+template <bool kContig>
+__device__ __forceinline__ PayloadRegs load_payload(const Lane &L, int64_t nblocks,
+                                                    const uint4 *__restrict__ codes,
                                                     const uint4 *__restrict__ micro,
                                                     const float *__restrict__ block) {
     PayloadRegs P;
-    const uint4 *src = codes + L.bl * 8 + L.q;
-    P.c0 = load_nt(src);
-    P.c1 = load_nt(src + 4);
+    if constexpr (kContig) {
+        // tile chunk 64 j + lane = chunk lane & 7 of block 8 j + (lane >> 3), clamped
+        // to the last block in a ragged tile; redeal_codes gives the lane layout
+        const int64_t last = nblocks - 1;
+        const int64_t b0 = L.tile + (L.lane >> 3), b1 = b0 + 8;
+        P.c0 = load_nt(codes + (b0 < last ? b0 : last) * 8 + (L.lane & 7));
+        P.c1 = load_nt(codes + (b1 < last ? b1 : last) * 8 + (L.lane & 7));
+    } else {
+        const uint4 *src = codes + L.bl * 8 + L.q;
+        P.c0 = load_nt(src);
+        P.c1 = load_nt(src + 4);
+    }
     const uint4 m = micro[L.bl];
     const unsigned sh = 16u * (L.q & 1);
     P.lo = ((L.q >> 1) ? m.y : m.x) >> sh;
     P.hi = ((L.q >> 1) ? m.w : m.z) >> sh;
     P.s = block[L.bl];
     return P;
+}
+
+// Contiguously loaded codes to the lane layout through the wavefront's LDS
+// region (at least 144 chunks, free): tile chunk c goes to chunk 9 (c >> 3) +
+// (c & 7) (a padding chunk per block keeps the reads free of bank conflicts),
+// and lane (p, q) reads chunks q and q + 4 of block p.
+__device__ __forceinline__ void redeal_codes(const Lane &L, uint4 *__restrict__ lds, PayloadRegs &P) {
+    wave_lds_sync();  // earlier reads of the region are done
+    uint4 *w = lds + 9 * (L.lane >> 3) + (L.lane & 7);
+    w[0] = P.c0;
+    w[72] = P.c1;
+    wave_lds_sync();
+    const uint4 *r = lds + 9 * L.p + L.q;
+    P.c0 = r[0];
+    P.c1 = r[4];
 }
 
 // Registers j = 0..63 get E2M1(code) * S_g (kSet), or the product is added to
@@ -715,10 +749,10 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_kernel(
     __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<kBf16>];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     float R[64];
-    const PayloadRegs P = load_payload(L, codes, micro, block);
+    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
+    const PayloadRegs P = load_payload<false>(L, nblocks, codes, micro, block);
     const bool fold = kFwht && fold_sixteenth(P.s);
     dequant<kSet>(P, R, fold ? 0.0625f : 1.0f);
-    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
     receiver_transform<kFwht, kBf16>(L, wl, R, fold);
     store_out<kBf16>(L, nblocks, wl, out, R);
 }
@@ -732,7 +766,8 @@ struct Peers {
 
 // Sum of k payloads into R (mode kFma or kAdd) with kInFlight payloads' loads
 // outstanding: the loads of peer p + kInFlight are issued as soon as peer p has
-// been dequantised.  k is wave-uniform, so every branch here is uniform.  One
+// been dequantised.  Codes are loaded contiguously and re-dealt through the
+// wavefront's LDS region lds (free during the sum, at least 144 chunks).  k is wave-uniform, so every branch here is uniform.  One
 // payload in flight measured best: every further buffer costs 12 registers, and
 // the resident wavefronts those registers would allow hide more latency.
 #ifndef FP4Q_PEERS_IN_FLIGHT
@@ -741,18 +776,21 @@ struct Peers {
 constexpr int kInFlight = FP4Q_PEERS_IN_FLIGHT;
 
 template <DequantMode kMode>
-__device__ __forceinline__ void sum_peers(const Lane &L, const Peers &peers, int k, float (&R)[64]) {
+__device__ __forceinline__ void sum_peers(const Lane &L, int64_t nblocks, const Peers &peers, int k,
+                                          uint4 *__restrict__ lds, float (&R)[64]) {
     PayloadRegs buf[kInFlight];
 #pragma unroll
     for (int i = 0; i < kInFlight; ++i)
-        if (i < k) buf[i] = load_payload(L, peers.codes[i], peers.micro[i], peers.block[i]);
+        if (i < k) buf[i] = load_payload<true>(L, nblocks, peers.codes[i], peers.micro[i], peers.block[i]);
     for (int p = 0; p < k; p += kInFlight) {
 #pragma unroll
         for (int i = 0; i < kInFlight; ++i) {
             if (p + i < k) {
+                redeal_codes(L, lds, buf[i]);
                 dequant<kMode>(buf[i], R);
                 const int nx = p + i + kInFlight;
-                if (nx < k) buf[i] = load_payload(L, peers.codes[nx], peers.micro[nx], peers.block[nx]);
+                if (nx < k)
+                    buf[i] = load_payload<true>(L, nblocks, peers.codes[nx], peers.micro[nx], peers.block[nx]);
             }
         }
     }
@@ -769,8 +807,8 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
     float R[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) R[j] = 0.0f;
-    sum_peers<kFma>(L, peers, k, R);
     uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
+    sum_peers<kFma>(L, nblocks, peers, k, wl, R);
     receiver_transform<kFwht, kBf16>(L, wl, R);
     store_out<kBf16>(L, nblocks, wl, out, R);
 }
@@ -829,7 +867,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
 #pragma unroll
         for (int j = 0; j < 64; ++j) R[j] = 0.0f;
     }
-    sum_peers<kAdd>(L, peers, k, R);
+    sum_peers<kAdd>(L, nblocks, peers, k, lds, R);
 
     float s, t[4];
     unsigned mw, C[8];
