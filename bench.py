@@ -483,6 +483,37 @@ def copy_reference(torch, dev):
     del src, dst
 
 
+def cold_timing(fp4q, torch, X, P, Y, reps: int = 10, flush_bytes: int = 2 << 30):
+    """Single launches from a cold cache: before each one, a read of flush_bytes
+    (a reduction over a buffer eight times the last-level cache) evicts what the
+    previous launch left and drains its write-back.  The kernel and its event
+    pair are queued right behind that read, so the host's launch latency never
+    falls inside the events.  Medians of `reps` launches."""
+    flush = torch.ones(flush_bytes // 8, dtype=torch.int64, device=X[0].device)
+    n = X[0].numel()
+    ab = algorithmic_bytes(n)
+    res = {}
+    for name, fn in (("compress", lambda: fp4q.fp4q_compress(X[0], *P[0])),
+                     ("decompress", lambda: fp4q.fp4q_decompress(*P[1], out=Y[0]))):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            flush.max()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        med = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+        gbps = ab[name] / med / 1e9
+        res[name] = {"median_us": round(med * 1e6, 2), "achieved_GBps": round(gbps, 1),
+                     "frac": round(gbps / PEAK_GBPS, 4)}
+        log("cold %-10s median %7.1f us  %7.1f GB/s  %.1f%% of HBM peak" % (
+            name, med * 1e6, gbps, 100 * gbps / PEAK_GBPS))
+    del flush
+    res["flush"] = "%d MiB read before each launch" % (flush_bytes >> 20)
+    return res
+
+
 def copy_ceiling(torch, dev, nbytes: int = 512 << 20, iters: int = 20):
     """A plain device-to-device copy (the runtime's copy kernel) between two
     buffers of nbytes, timed with HIP events: the GB/s (bytes read + written)
@@ -727,6 +758,7 @@ def main():
         "rel_rmse": {"fwht": round(rmse, 6), "no_fwht": round(rmse_nf, 6)},
     }
     result["variants"] = variant_timing(fp4q, torch, X, P, Y)
+    result["cold"] = cold_timing(fp4q, torch, X, P, Y)
     # the copy ceiling's 512 MiB copies would join the counter-scale reference's
     # 256 MiB copies in a --copy-reference run (the summary takes the largest copies)
     if not args.copy_reference:
