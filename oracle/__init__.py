@@ -69,6 +69,9 @@ def lib():
         L.fp4q_ref_e2m1_encode_n.argtypes = [P, I64, P]
         L.fp4q_ref_e4m3_encode_n.argtypes = [P, I64, P]
         L.fp4q_ref_fwht256_n.argtypes = [P, I64]
+        L.fp4q_ref_bf16_round.argtypes = [ctypes.c_float]
+        L.fp4q_ref_bf16_round.restype = ctypes.c_uint16
+        L.fp4q_ref_bf16_round_n.argtypes = [P, I64, P]
         _lib = L
     return _lib
 
@@ -183,6 +186,15 @@ def fwht256(y: np.ndarray) -> np.ndarray:
         raise ValueError("size must be a multiple of 256")
     lib().fp4q_ref_fwht256_n(_ptr(y), y.size // BLOCK)
     return y
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """The bfloat16 output option: float32 values rounded to the nearer
+    neighbouring bfloat16 (ties to even), as uint16 bit patterns."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().fp4q_ref_bf16_round_n(_ptr(x), x.size, _ptr(out))
+    return out
 
 
 def widen(x_bf16: np.ndarray) -> np.ndarray:

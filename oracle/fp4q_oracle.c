@@ -389,6 +389,24 @@ void fp4q_ref_decompress_mx(const uint8_t *codes, const uint8_t *scales, int64_t
     }
 }
 
+/* ------------------------------------------------ bfloat16 output option
+ * The receiver may write bfloat16 instead of binary32: each binary32 result is
+ * rounded to the nearer of its two neighbouring bfloat16 values (the one that
+ * keeps its top 16 bits, and the next one away from zero), ties to the even
+ * significand.  Past the largest finite bfloat16 the next value is taken as
+ * 2^128, so that overflow rounds as IEEE rounding does.  Finite inputs. */
+uint16_t fp4q_ref_bf16_round(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t lo = (uint16_t)(u >> 16), hi = (uint16_t)(lo + 1);
+    if ((u & 0xFFFFu) == 0) return lo;                    /* already a bfloat16 */
+    double x = fabs((double)f), a = fabs((double)widen_bf16(lo));
+    double b = ((hi & 0x7F80u) == 0x7F80u) ? ldexp(1.0, 128) : fabs((double)widen_bf16(hi));
+    if (x - a < b - x) return lo;
+    if (x - a > b - x) return hi;
+    return (lo & 1u) ? hi : lo;
+}
+
 /* ------------------------------------------------- vectorised scalar helpers */
 void fp4q_ref_e2m1_encode_n(const float *v, int64_t n, uint8_t *out) {
 #pragma omp parallel for schedule(static) num_threads(g_threads)
@@ -402,4 +420,9 @@ void fp4q_ref_e4m3_encode_n(const float *t, int64_t n, uint8_t *out) {
 
 void fp4q_ref_fwht256_n(float *y, int64_t nblocks) {
     for (int64_t b = 0; b < nblocks; ++b) fp4q_ref_fwht256(y + BLOCK * b);
+}
+
+void fp4q_ref_bf16_round_n(const float *x, int64_t n, uint16_t *out) {
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t i = 0; i < n; ++i) out[i] = fp4q_ref_bf16_round(x[i]);
 }

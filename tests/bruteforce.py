@@ -93,3 +93,26 @@ def near(values: np.ndarray, points: np.ndarray, rel: float) -> np.ndarray:
     idx = np.clip(np.searchsorted(points, a), 1, len(points) - 1)
     d = np.minimum(np.abs(a - points[idx - 1]), np.abs(a - points[idx]))
     return d <= rel * np.maximum(a, 1e-300)
+
+
+def bf16_magnitudes() -> np.ndarray:
+    """Every non-negative finite bfloat16 value in code order (codes 0 .. 0x7F7F),
+    then 2^128 standing in for the infinity past the largest one."""
+    codes = np.arange(0x7F80, dtype=np.uint32)
+    vals = (codes << 16).view(np.float32).astype(np.float64)
+    return np.append(vals, 2.0 ** 128)
+
+
+def nearest_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 by searching the whole grid of bfloat16
+    values: the nearer neighbour of |x|, ties to the even code; the sign is
+    copied.  uint16 bit patterns."""
+    x = np.asarray(x, np.float32).reshape(-1)
+    table = bf16_magnitudes()
+    m = np.abs(x.astype(np.float64))
+    i = np.searchsorted(table, m, side="right") - 1          # table[i] <= m < table[i + 1]
+    i = np.minimum(i, table.size - 2)
+    d_lo, d_hi = m - table[i], table[i + 1] - m
+    code = np.where(d_lo < d_hi, i, np.where(d_hi < d_lo, i + 1, np.where(i % 2 == 0, i, i + 1)))
+    code = np.where(d_lo == 0, i, code)
+    return (code.astype(np.uint16) | np.where(np.signbit(x), 0x8000, 0).astype(np.uint16))

@@ -66,7 +66,7 @@ def run_compress_decompress(fp4q, xb, fwht=True, name=""):
     np.testing.assert_array_equal(o.view(np.uint32), want.view(np.uint32))
     parity.check_rowwise(o, want)
     ob = out_bf.cpu().view(torch.int16).numpy().view(np.uint16)
-    np.testing.assert_array_equal(ob, inputs.f32_to_bf16_bits(want))
+    np.testing.assert_array_equal(ob, oracle.round_bf16(want))
     return stats
 
 
@@ -225,7 +225,7 @@ def run_mx(fp4q, xb, fwht, name):
     want = oracle.decompress_mx(ref["codes"], ref["scales"], fwht=fwht)
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
     np.testing.assert_array_equal(outb.cpu().view(torch.int16).numpy().view(np.uint16),
-                                  inputs.f32_to_bf16_bits(want))
+                                  oracle.round_bf16(want))
 
 
 @pytest.mark.parametrize("fwht", [True, False])
@@ -369,7 +369,7 @@ def test_offsets_beyond_32_bits(fp4q):
     out.mul_(2.0)
     assert torch.equal(acc, out)
     ob = acc_bf.index_select(0, pick_d).cpu().view(torch.int16).numpy().view(np.uint16)
-    np.testing.assert_array_equal(ob, inputs.f32_to_bf16_bits(2.0 * want))
+    np.testing.assert_array_equal(ob, oracle.round_bf16(2.0 * want))
     assert n > (1 << 32)
     del acc, acc_bf, out, c, m, b
     torch.cuda.empty_cache()
@@ -546,7 +546,7 @@ def test_random_sweep(fp4q, chunk):
         want = oracle.decompress(ref["codes"], ref["micro"], ref["block"], fwht=fwht)
         np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
         np.testing.assert_array_equal(outb.cpu().view(torch.int16).numpy().view(np.uint16),
-                                      inputs.f32_to_bf16_bits(want))
+                                      oracle.round_bf16(want))
         # MX round trip
         rmx = oracle.compress_mx(xb, fwht=fwht, debug=True)
         mc, ms = fp4q.fp4q_compress_mx(to_dev(xb), flags=flags)

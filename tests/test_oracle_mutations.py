@@ -19,7 +19,8 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_TESTS = ["tests/test_oracle_formats.py", "tests/test_oracle_fwht.py",
              "tests/test_oracle_pipeline.py", "tests/test_oracle_requantize.py",
-             "tests/test_oracle_mx.py", "tests/test_oracle_properties.py"]
+             "tests/test_oracle_mx.py", "tests/test_oracle_properties.py",
+             "tests/test_oracle_bf16.py"]
 
 # name -> (text in the oracle source, its replacement); the text must occur once
 MUTANTS = {
@@ -72,6 +73,9 @@ MUTANTS = {
     "re-quantise: local slice not transformed": ("if (fwht) fp4q_ref_fwht256(acc);", ""),
     "re-quantise: first peer skipped": ("for (int p = 0; p < k; ++p) {\n            decompress_block(",
                                         "for (int p = 1; p < k; ++p) {\n            decompress_block("),
+    # bfloat16 output option
+    "bf16 round: ties away from zero": ("return (lo & 1u) ? hi : lo;", "return hi;"),
+    "bf16 round: truncation": ("if (x - a < b - x) return lo;", "if (x - a < b - x || 1) return lo;"),
     # MX variant
     "mx: scale exponent off by one": ("int e = (e2 - 1) - 2;", "int e = (e2 - 1) - 1;"),
     "mx: zero group exponent": ("if (!(amax > 0.0f)) return -127;", "if (!(amax > 0.0f)) return 0;"),
