@@ -66,8 +66,9 @@ constexpr int kWave = 64;
 constexpr int kTileBlocks = 16;  // 256-blocks per wavefront
 // Wavefronts per workgroup (all LDS use is per wavefront).  The compute-heavy
 // sender runs best with one wavefront per workgroup (more resident waves per
-// CU); the store-heavy receiver with four (neighbouring tiles write
-// neighbouring output from one CU).
+// CU); the store-heavy receivers with four (neighbouring tiles write
+// neighbouring output from one CU), except decompress with bf16 output, which
+// is compute-heavy too (kDecompressWaves).
 #ifndef FP4Q_SENDER_WAVES
 #define FP4Q_SENDER_WAVES 1
 #endif
