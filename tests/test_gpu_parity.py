@@ -324,7 +324,8 @@ def test_offsets_beyond_32_bits(fp4q):
     wrong place changes a sampled row.  Sampled rows on both sides of every
     boundary are checked against the oracle; accumulate([P, P]) must equal
     2 x decompress(P) bit for bit over the whole tensor (the sum of two equal
-    exact products is exact)."""
+    exact products is exact), and the re-quantisation of [P, P] matches the
+    oracle on the sampled rows."""
     L, src_rows = 4096, 1024
     rows = (1 << 20) + 256
     n = rows * L
@@ -370,8 +371,16 @@ def test_offsets_beyond_32_bits(fp4q):
     assert torch.equal(acc, out)
     ob = acc_bf.index_select(0, pick_d).cpu().view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(ob, oracle.round_bf16(2.0 * want))
+    del acc, acc_bf, out
+    # the re-quantisation of two copies of the payload (peer codes read past 2^31
+    # bytes, by the multi-peer kernels' contiguous loads): sampled rows
+    rq = fp4q.fp4q_reduce_requantize([(c, m, b), (c, m, b)])
+    torch.cuda.synchronize()
+    got_rq = [t.index_select(0, pick_d).cpu().numpy() for t in rq]
+    st = parity.check_compress(got_rq, oracle.requantize([tuple(got)] * 2, debug=True))
+    assert st["code_mismatch"] == 0 and st["micro_mismatch"] == 0
     assert n > (1 << 32)
-    del acc, acc_bf, out, c, m, b
+    del rq, c, m, b
     torch.cuda.empty_cache()
 
 
