@@ -363,6 +363,7 @@ def variant_timing(fp4q, torch, X, P, Y, iters: int = 40):
         ("decompress_no_fwht", lambda s: fp4q.fp4q_decompress(*P[s], out=Y[s], flags=nf), pay + 4 * n),
         ("compress_mx", lambda s: fp4q.fp4q_compress_mx(X[s], *MX[s]), 2 * n + mx_pay),
         ("decompress_mx", lambda s: fp4q.fp4q_decompress_mx(*MX[s], out=Y[s]), mx_pay + 4 * n),
+        ("decompress_mx_bf16_out", lambda s: fp4q.fp4q_decompress_mx(*MX[s], out=Yb[s]), mx_pay + 2 * n),
     )
     res = {}
     for name, fn, nbytes in cases:
