@@ -2,7 +2,6 @@
 roofline uses, the single-GPU guard, and the rocprofv3 summaries that the
 committed profiles and the bench line's `traffic` come from."""
 import csv
-import os
 import subprocess
 import sys
 
