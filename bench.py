@@ -600,24 +600,27 @@ def copy_ceiling(torch, dev, nbytes: int = 512 << 20, iters: int = 20):
 
 def graph_timed_steps(torch, fp4q, step, X, P, Y, S, args, min_steps: int = 40):
     """The timed steps as replays of a HIP graph of m steps (m a multiple of the
-    S buffer sets, at least min_steps): on tensors this small, launching from
-    Python would take longer than the kernels.  Per-kernel durations: HIP events
-    around replays of graphs of m compress launches and of m decompress launches
-    on the same rotation, divided by m."""
+    S buffer sets, at least min_steps), then one replay of a graph of the
+    remaining K mod m steps, so exactly K steps are timed: on tensors this small,
+    launching from Python would take longer than the kernels.  Per-kernel
+    durations: HIP events around replays of graphs of m compress launches and of
+    m decompress launches on the same rotation, divided by m."""
     m = S * -(-min_steps // S)
 
-    def capture(fn):
+    def capture(fn, count=m):
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                for i in range(m):
+                for i in range(count):
                     fn(i)
         torch.cuda.current_stream().wait_stream(side)
         return g
 
     g_step = capture(step)
+    reps, rest = divmod(args.steps, m)
+    g_rest = capture(step, rest) if rest else None   # continues the rotation: m % S == 0
     g_c = capture(lambda i: fp4q.fp4q_compress(X[i % S], *P[i % S]))
     g_d = capture(lambda i: fp4q.fp4q_decompress(*P[(i % S - 1) % S], out=Y[i % S]))
     torch.cuda.synchronize()
@@ -625,10 +628,11 @@ def graph_timed_steps(torch, fp4q, step, X, P, Y, S, args, min_steps: int = 40):
     for _ in range(-(-args.warmup // m)):
         g_step.replay()
     torch.cuda.synchronize()
-    reps = -(-args.steps // m)
     t0 = time.perf_counter()
     for _ in range(reps):
         g_step.replay()
+    if g_rest is not None:
+        g_rest.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = {}
@@ -642,9 +646,9 @@ def graph_timed_steps(torch, fp4q, step, X, P, Y, S, args, min_steps: int = 40):
             b.record()
         torch.cuda.synchronize()
         per[name] = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3 / m
-    timing = ("HIP graph replays of %d steps; per-kernel: HIP events around replays of graphs of %d "
-              "launches of each kernel, divided by %d" % (m, m, m))
-    return reps * m, wall, per["compress"], per["decompress"], timing
+    timing = ("HIP graph replays of %d steps (and one of the remaining %d); per-kernel: HIP events "
+              "around replays of graphs of %d launches of each kernel, divided by %d" % (m, rest, m, m))
+    return args.steps, wall, per["compress"], per["decompress"], timing
 
 
 def main():
