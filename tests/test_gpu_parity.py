@@ -317,6 +317,23 @@ def test_concurrent_streams(fp4q):
             assert torch.equal(res[i][1], ref_out[i])
 
 
+def test_stacked_tensors_give_stacked_payloads(fp4q):
+    """Tensors of one row length stacked into one call: the payload of the stack
+    is the payloads of its parts end to end (blocks never straddle rows and every
+    payload array is flat in block order), and so is the decompressed output."""
+    parts = [inputs.make_normal(r, 4096, seed=40 + i) for i, r in enumerate((37, 2048, 5))]
+    pd = [to_dev(p) for p in parts]
+    stack = torch.cat(pd, 0)
+    whole = fp4q.fp4q_compress(stack)
+    each = [fp4q.fp4q_compress(p) for p in pd]
+    out_whole = fp4q.fp4q_decompress(*whole)
+    out_each = [fp4q.fp4q_decompress(*e) for e in each]
+    torch.cuda.synchronize()
+    for k in range(3):
+        assert torch.equal(whole[k].view(torch.uint8), torch.cat([e[k] for e in each], 0).view(torch.uint8))
+    assert torch.equal(out_whole.view(torch.int32), torch.cat(out_each, 0).view(torch.int32))
+
+
 def test_offsets_beyond_32_bits(fp4q):
     """N = 2^32 + 2^20 elements (rows of 4096): input, code, micro-scale and output
     offsets all pass 2^31 and 2^32 bytes in the tail.  The tensor is a seeded
