@@ -1249,7 +1249,7 @@ const char *fp4q_status_str(int status) {
         case FP4Q_ERR_NULL: return "null pointer";
         case FP4Q_ERR_SHAPE: return "bad shape (rows >= 0, row_len > 0 and a multiple of 256)";
         case FP4Q_ERR_ALIGN: return "misaligned pointer (16 bytes; 4 for scales)";
-        case FP4Q_ERR_K: return "peer count outside 1..16";
+        case FP4Q_ERR_K: return "peer count outside 1..16 (0..16 with a local slice)";
         case FP4Q_ERR_ARG: return "bad flags, output type, or overlapping buffers";
         case FP4Q_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown status";
