@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "fp4q.hip")]
-HEADER = os.path.join(ROOT, "include", "fp4q.h")
+HEADERS = [os.path.join(ROOT, "include", "fp4q.h"), os.path.join(HERE, "csrc", "fp4q_numerics.h")]
 LIB = os.path.join(HERE, "libfp4q.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,7 +30,7 @@ HIPCC_FLAGS = [
 
 def build(force: bool = True, verbose: bool = False) -> str:
     stale = not os.path.exists(LIB) or any(
-        os.path.getmtime(s) > os.path.getmtime(LIB) for s in SOURCES + [HEADER])
+        os.path.getmtime(s) > os.path.getmtime(LIB) for s in SOURCES + HEADERS)
     if not (force or stale):
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()

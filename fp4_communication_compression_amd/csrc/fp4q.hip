@@ -59,6 +59,7 @@
 #include <utility>
 
 #include "fp4q.h"
+#include "fp4q_numerics.h"
 
 namespace {
 
@@ -229,20 +230,14 @@ __device__ __forceinline__ void swap_lane5(float (&R)[64]) {
         if ((j & H) == 0) swap32(R[j], R[j | H]);
 }
 
-// Correctly rounded 1/x for 2^-125 <= |x| < 2^125: hardware estimate and one
-// Newton step (checked against IEEE division for every fp32 in that range).
-__device__ __forceinline__ float rcp_rn(float x) {
-    const float y = __builtin_amdgcn_rcpf(x);
-    const float e = fmaf(-x, y, 1.0f);
-    return fmaf(e, y, y);
-}
-// a / b rounded to nearest from y = rcp_rn(b) with one remainder correction;
-// the remainder a - q b is exact for a >= 2^-99 and normal b.
-__device__ __forceinline__ float div_rn(float a, float b, float y) {
-    const float q = a * y;
-    const float r = fmaf(-q, b, a);
-    return fmaf(r, y, q);
-}
+using fp4q_num::coarse_scale;
+using fp4q_num::div_rn;
+using fp4q_num::e2m1_pair;
+using fp4q_num::e2m1_values;
+using fp4q_num::e4m3_pair;
+using fp4q_num::e4m3_value;
+using fp4q_num::kE4M3Max;
+using fp4q_num::rcp_rn;
 
 // Maximum of v over the four lanes of a block (lane bits 4 and 5).
 __device__ __forceinline__ float block_lane_max(float v) {
@@ -264,14 +259,7 @@ __device__ __forceinline__ void transpose4(T &x0, T &x1, T &x2, T &x3) {
     swap32(x1, x3);
 }
 
-// Two fp32 values rounded to nearest-even bf16, lo in the low half: one
-// v_cvt_pk_bf16_f32 (denormals kept, as the whole library is built).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ unsigned bf16_rne_pair(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
+using fp4q_num::bf16_rne_pair;
 
 // Wave-private LDS staging: a wavefront exchanges data among its own lanes
 // through a region of 16-byte chunks (no workgroup barrier is needed; the
@@ -389,26 +377,24 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
 
     float inv[4];
     if (A >= 0x1p-80f) {
-        s = div_rn(A, 2688.0f, 1.0f / 2688.0f);
+        s = coarse_scale(A);
         const float d6 = 6.0f * s;
         const float y = rcp_rn(d6);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), 448.0f);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+        for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), kE4M3Max);
+        mw = e4m3_pair<true>(e4m3_pair<false>(0u, t[0], t[1]), t[2], t[3]);
         static_for<4>([&](auto k) {
-            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+            const float S = s * e4m3_value<decltype(k)::value>(mw);
             inv[k] = (S == 0.0f) ? 0.0f : rcp_rn(S);
         });
     } else {  // tiny or zero block: IEEE division throughout
-        s = A / 2688.0f;
+        s = A / fp4q_num::kScaleDivisor;
         const float d6 = 6.0f * s;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, 448.0f) : 0.0f;
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+        for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, kE4M3Max) : 0.0f;
+        mw = e4m3_pair<true>(e4m3_pair<false>(0u, t[0], t[1]), t[2], t[3]);
         static_for<4>([&](auto k) {
-            const float S = s * __builtin_amdgcn_cvt_f32_fp8(mw, decltype(k)::value);
+            const float S = s * e4m3_value<decltype(k)::value>(mw);
             inv[k] = fminf((S == 0.0f) ? 0.0f : 1.0f / S, FLT_MAX);
         });
     }
@@ -424,8 +410,7 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
         unsigned c = as_u(R[8 * w]);
         static_for<4>([&](auto sel) {
             const int j = 8 * w + 2 * decltype(sel)::value;
-            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j] * r, R[j + 1] * r, 1.0f,
-                                                         decltype(sel)::value);
+            c = e2m1_pair<decltype(sel)::value>(c, R[j] * r, R[j + 1] * r);
         });
         C[w] = c;
     }
@@ -531,8 +516,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
 
     // micro-scales: quarter q holds groups q + 4k; make it groups 4q .. 4q + 3
     transpose4(t[0], t[1], t[2], t[3]);
-    mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-    mw = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], mw, true);
+    mw = e4m3_pair<true>(e4m3_pair<false>(0u, t[0], t[1]), t[2], t[3]);
 
     wave_lds_sync();  // every lane has read its chunks from the region
     store_codes<true>(L, nblocks, lds, codes, C);
@@ -612,15 +596,13 @@ enum DequantMode { kSet, kFma, kAdd };
 template <DequantMode kMode>
 __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64], float dscale = 1.0f) {
     const unsigned C[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
-    const float S[4] = {P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 0),
-                        P.s * __builtin_amdgcn_cvt_f32_fp8(P.lo, 1),
-                        P.s * __builtin_amdgcn_cvt_f32_fp8(P.hi, 0),
-                        P.s * __builtin_amdgcn_cvt_f32_fp8(P.hi, 1)};
+    const float S[4] = {P.s * e4m3_value<0>(P.lo), P.s * e4m3_value<1>(P.lo),
+                        P.s * e4m3_value<0>(P.hi), P.s * e4m3_value<1>(P.hi)};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const float Sg = S[w >> 1];
         static_for<4>([&](auto sel) {
-            const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], dscale, decltype(sel)::value);
+            const auto f = e2m1_values<decltype(sel)::value>(C[w], dscale);
             const int j = 8 * w + 2 * decltype(sel)::value;
             if constexpr (kMode == kFma) {
                 R[j] = fmaf(f[0], Sg, R[j]);
@@ -950,7 +932,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
         unsigned c = as_u(R[8 * w]);  // every byte is written below (as in compress)
         static_for<4>([&](auto sel) {
             const int j = 8 * w + 2 * decltype(sel)::value;
-            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, R[j], R[j + 1], sc, decltype(sel)::value);
+            c = e2m1_pair<decltype(sel)::value>(c, R[j], R[j + 1], sc);
         });
         C[w] = c;
     }
@@ -991,7 +973,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void decompress_mx_kernel(
 #pragma unroll
         for (int w = 4 * h; w < 4 * h + 4; ++w) {
             static_for<4>([&](auto sel) {
-                const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(C[w], sc, decltype(sel)::value);
+                const auto f = e2m1_values<decltype(sel)::value>(C[w], sc);
                 const int j = 8 * w + 2 * decltype(sel)::value;
                 R[j] = f[0];
                 R[j + 1] = f[1];
