@@ -97,7 +97,7 @@ def test_counter_summary_reference_is_the_largest_copies(tmp_path):
         bench.summarize_counters(fetch, no_ref)
 
 
-def test_trace_summary(tmp_path):
+def test_trace_summary(tmp_path, monkeypatch):
     d = tmp_path / "t" / "host"
     d.mkdir(parents=True)
     fields = ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp", "End_Timestamp"]
@@ -105,7 +105,7 @@ def test_trace_summary(tmp_path):
         w = csv.DictWriter(f, fields)
         w.writeheader()
         t = 0
-        for grid, us in [(G, 100), (G, 110), (G, 120), (G // 8, 5)]:   # ns timestamps
+        for grid, us in [(G, 90), (G, 100), (G, 110), (G // 8, 5), (G, 120), (G, 130)]:   # ns timestamps
             w.writerow({"Kernel_Name": DECOMP, "Grid_Size_X": grid, "Grid_Size_Y": 1, "Grid_Size_Z": 1,
                         "Start_Timestamp": t, "End_Timestamp": t + us * 1000})
             t += 10 ** 6
@@ -113,11 +113,14 @@ def test_trace_summary(tmp_path):
                     "Grid_Size_Z": 1, "Start_Timestamp": 0, "End_Timestamp": 5})
     text = bench.summarize_trace(str(tmp_path / "t"))
     rows = [l for l in text.splitlines() if l.startswith("| decompress_kernel")]
-    assert rows == ["| decompress_kernel<true, false> | %d | 3 | 110.00 | 110.00 | 100.00 | 120.00 |" % G]
-    assert "some_other_kernel" not in text and "Timed region" not in text
-    # the timed region of a 2-step run: the two full-size launches before the last one
+    assert rows == ["| decompress_kernel<true, false> | %d | 5 | 110.00 | 110.00 | 90.00 | 130.00 |" % G]
+    assert "some_other_kernel" not in text and "per-kernel pass" not in text
+    # a 2-step run with a 2-step per-kernel pass: the last two full-size launches
+    # are the pass, the two before them the timed region
+    monkeypatch.setattr(bench, "KERNEL_PASS", 2)
     text = bench.summarize_trace(str(tmp_path / "t"), timed_steps=2)
-    assert "| decompress_kernel<true, false> | 2 | 105.00 | 105.00 |" in text
+    assert "| decompress_kernel<true, false> | per-kernel pass | 2 | 125.00 | 125.00 |" in text
+    assert "| decompress_kernel<true, false> | timed region | 2 | 105.00 | 105.00 |" in text
 
 
 def test_traffic_is_read_only_for_the_current_kernel_source(tmp_path, monkeypatch):
