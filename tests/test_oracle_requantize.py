@@ -145,3 +145,106 @@ def test_requantize_error_bound_and_meaning():
     dec = oracle.decompress_f64(got["codes"], got["micro"], got["block"])
     rel = np.linalg.norm(dec - ref) / np.linalg.norm(ref)
     assert rel < 0.2
+
+
+U = 2.0 ** -24   # unit roundoff of binary32
+
+
+def _exact_value(codes, micro, block):
+    """A payload's exact value in binary64, by the format definition: E2M1 grid
+    value x block scale x E4M3 value (2 + 24 + 4 significant bits: exact)."""
+    c = unpack(codes).reshape(-1, 16, 16)
+    mag = bf.E2M1_GRID[c & 7] * np.where(c & 8, -1.0, 1.0)
+    S = np.asarray(block, np.float64).reshape(-1, 1) * bf.E4M3_VALUES[np.asarray(micro).reshape(-1, 16)]
+    return (mag * S[:, :, None]).reshape(-1, 256)
+
+
+@pytest.mark.parametrize("local", [False, True])
+@pytest.mark.parametrize("fwht", [True, False])
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_requantize_is_compress_of_the_exact_sum(k, fwht, local):
+    """The plain definition of the reduce-scatter receiver: decompress every
+    peer's payload exactly (binary64, its inverse transform a dense H/16), add
+    the rank's own slice, and compress the sum -- transform (dense H/16 in
+    binary64), block and micro-scales, E2M1 codes by nearest-code search.  The
+    oracle computes the same in binary32 in the transform domain; its result
+    must match wherever the exact value lies outside the band that binary32
+    rounding can move it by.  Per element that band is at most
+    (k + 3) u (sum over peers of |term| + |local term|) + 9 u sum_j |x_j| / 16
+    (two roundings per decoded term, k + 1 additions, eight radix-2 stages of the
+    local slice's transform), u = 2^-24, widened by 1 %; block scales, group
+    maxima and quotients carry it into the micro-scale and code comparisons."""
+    rows, L = 6, 1024
+    pay, exact_terms = [], []
+    for p in range(k):
+        r = oracle.compress(inputs.make_normal(rows, L, seed=300 + p, scale=1e-3), fwht=fwht)
+        pay.append((r["codes"], r["micro"], r["block"]))
+        exact_terms.append(_exact_value(r["codes"], r["micro"], r["block"]))   # transform domain
+    H = bf.H256.astype(np.float64) / 16.0
+    T = (lambda z: z @ H.T) if fwht else (lambda z: z)
+    signal = sum(T(t) for t in exact_terms)          # sum of the decompressed peers (H/16 self-inverse)
+    xb = inputs.make_normal(rows, L, seed=399, scale=1e-3) if local else None
+    if local:
+        signal = signal + oracle.widen(xb).astype(np.float64).reshape(-1, 256)
+    y = T(signal)                                    # compress: the transform of the exact sum
+    got = oracle.requantize(pay, local=xb, fwht=fwht, debug=True)
+
+    # the binary32 band
+    mag = sum(np.abs(t) for t in exact_terms)
+    E = (k + 3) * U * mag
+    if local:
+        xl = np.abs(oracle.widen(xb).astype(np.float64).reshape(-1, 256))
+        E = E + (k + 3) * U * np.abs(T(oracle.widen(xb).astype(np.float64).reshape(-1, 256)))
+        E = E + (9 * U * xl.sum(axis=1, keepdims=True) / 16.0 if fwht else 0.0)
+    E = 1.01 * E
+
+    A = np.abs(y).max(axis=1)
+    EA = E.max(axis=1)
+    s = A / 2688.0
+    np.testing.assert_array_less(np.abs(got["block"].reshape(-1) - s), EA / 2688.0 + 2 * U * s + 1e-300)
+    yg, Eg = np.abs(y).reshape(-1, 16, 16), E.reshape(-1, 16, 16)
+    a = yg.max(axis=2)
+    t = a / (6.0 * s[:, None])
+    rel_t = Eg.max(axis=2) / np.maximum(a, 1e-300) + EA[:, None] / A[:, None] + 4 * U
+    m = bf.nearest_e4m3(t)
+    mids = bf.e4m3_midpoints()
+    idx = np.clip(np.searchsorted(mids, t), 1, len(mids) - 1)
+    dmid = np.minimum(np.abs(t - mids[idx - 1]), np.abs(t - mids[idx]))
+    near_m = dmid <= rel_t * t + 1e-6 * t
+    gm = got["micro"].reshape(-1, 16)
+    assert np.all((gm == m) | near_m), "micro-scales differ away from a midpoint"
+    S = s[:, None] * bf.E4M3_VALUES[m]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(S[:, :, None] > 0, y.reshape(-1, 16, 16) / S[:, :, None], 0.0)
+        dv = np.where(S[:, :, None] > 0, np.abs(v) * (EA[:, None, None] / A[:, None, None] + 4 * U)
+                      + Eg / S[:, :, None], 0.0)
+    want = bf.nearest_e2m1(v).reshape(-1, 256)
+    bnd = bf.e2m1_boundaries()
+    av = np.abs(v).reshape(-1, 256)
+    idx = np.clip(np.searchsorted(bnd, av), 1, len(bnd) - 1)
+    dist = np.minimum(np.abs(av - bnd[idx - 1]), np.abs(av - bnd[idx]))
+    near_c = (dist <= dv.reshape(-1, 256) + 1e-6 * av) | np.repeat(near_m | (gm != m), 16, axis=1)
+    gc = unpack(got["codes"]).reshape(-1, 256)
+    # a zero exact value may come out as a rounded residue of either sign
+    ok = (gc == want) | near_c | (((gc & 7) == 0) & ((want & 7) == 0))
+    assert np.all(ok), "codes differ away from a rounding boundary"
+    assert near_c.mean() < 0.01, "the binary32 band exempts too much to pin anything"
+
+
+def test_requantize_sums_in_peer_order_from_zero():
+    """Peers are added to a +0 accumulator in order p = 0 .. k-1: a payload
+    followed by its negation cancels exactly (x + (-x) = +0), so [P, -P, Q]
+    re-quantises bit for bit as [Q] alone -- in any other order the large terms
+    of P would round away part of Q's small ones."""
+    big = oracle.compress(inputs.make_normal(6, 1024, seed=501))
+    small = oracle.compress(inputs.make_normal(6, 1024, seed=502, scale=1e-5))
+    P = (big["codes"], big["micro"], big["block"])
+    negP = ((big["codes"] ^ 0x88).astype(np.uint8), big["micro"], big["block"])
+    Q = (small["codes"], small["micro"], small["block"])
+    a = oracle.requantize([P, negP, Q])
+    b = oracle.requantize([Q])
+    for key in ("codes", "micro", "block"):
+        np.testing.assert_array_equal(a[key], b[key])
+    # the same three peers in reverse order do not cancel exactly
+    c = oracle.requantize([Q, negP, P])
+    assert any(not np.array_equal(c[key], b[key]) for key in ("codes", "micro", "block"))
