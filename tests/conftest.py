@@ -8,4 +8,4 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
-    config.addinivalue_line("markers", "slow: long CPU test (set FP4Q_SLOW=1 to run)")
+    config.addinivalue_line("markers", "exhaustive: sweeps every fp32 pattern of a range (CPU, about a minute)")

@@ -14,6 +14,14 @@ from tests import bruteforce as bf
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "e2m1_e4m3_values.txt")
 
 
+@pytest.fixture
+def all_threads():
+    """The exhaustive sweeps run the oracle on every host core."""
+    oracle.set_threads(os.cpu_count() or 1)
+    yield
+    oracle.set_threads(1)
+
+
 def _golden():
     e2m1, e4m3 = None, {}
     for line in open(GOLDEN):
@@ -64,6 +72,21 @@ def _windows(points: np.ndarray, half: int) -> np.ndarray:
     return w[w >= 0].astype(np.uint32).view(np.float32)
 
 
+def _exhaustive_runs(encode, brute, lo: int, hi: int, chunk: int = 1 << 24):
+    """Every fp32 bit pattern in [lo, hi) (all of one sign, so the magnitude grows
+    with the pattern): the oracle's code equals the brute-force code at each one.
+    The brute force (nearest value on an ordered grid, ties to the even code, the
+    sign copied) is monotone in the magnitude, so it is evaluated at both ends of
+    every run of equal oracle codes: equal there means equal on the whole run.
+    The oracle itself runs on every pattern."""
+    for b in range(lo, hi, chunk):
+        u = np.arange(b, min(hi, b + chunk), dtype=np.uint32)
+        c = encode(u.view(np.float32))
+        cut = np.flatnonzero(c[1:] != c[:-1])
+        ends = np.concatenate([[0], cut, cut + 1, [c.size - 1]])
+        np.testing.assert_array_equal(brute(u[ends].view(np.float32)), c[ends])
+
+
 def test_e2m1_encode_exhaustive_near_every_decision_point():
     """All fp32 patterns within 2^16 ulps of every midpoint and grid value, both signs."""
     pts = np.concatenate([bf.e2m1_boundaries(), bf.E2M1_GRID[1:]]).astype(np.float32)
@@ -72,12 +95,12 @@ def test_e2m1_encode_exhaustive_near_every_decision_point():
         np.testing.assert_array_equal(oracle.e2m1_encode(s_), bf.nearest_e2m1(s_))
 
 
-@pytest.mark.skipif(os.environ.get("FP4Q_SLOW") != "1", reason="set FP4Q_SLOW=1")
-@pytest.mark.slow
+@pytest.mark.exhaustive
 @pytest.mark.parametrize("lo,hi", [(0x3E000000, 0x3F800000), (0x3F800000, 0x40800000),
                                    (0x40800000, 0x41800000)])
-def test_e2m1_encode_exhaustive_binades(lo, hi):
-    """Every fp32 pattern with magnitude in [1/8, 16), both signs, against brute force."""
+def test_e2m1_encode_exhaustive_binades(lo, hi, all_threads):
+    """Every fp32 pattern with magnitude in [1/8, 16), both signs, against the full
+    nearest-code search at every pattern (no shortcut)."""
     step = 1 << 22
     for b in range(lo, hi, step):
         v = _all_patterns(b, min(hi, b + step))
@@ -94,14 +117,11 @@ def test_e2m1_encode_random_patterns():
     np.testing.assert_array_equal(oracle.e2m1_encode(v), bf.nearest_e2m1(v))
 
 
-@pytest.mark.skipif(os.environ.get("FP4Q_SLOW") != "1", reason="set FP4Q_SLOW=1")
-@pytest.mark.slow
-def test_e2m1_encode_exhaustive_all_finite():
-    step = 1 << 24
-    for b in range(0, 0x7F800000, step):
-        v = _all_patterns(b, min(0x7F800000, b + step))
-        for s in (v, -v):
-            np.testing.assert_array_equal(oracle.e2m1_encode(s), bf.nearest_e2m1(s))
+@pytest.mark.exhaustive
+def test_e2m1_encode_exhaustive_all_finite(all_threads):
+    """Every finite fp32 bit pattern, both signs (2^32 - 2^25 patterns)."""
+    _exhaustive_runs(oracle.e2m1_encode, bf.nearest_e2m1, 0x00000000, 0x7F800000)
+    _exhaustive_runs(oracle.e2m1_encode, bf.nearest_e2m1, 0x80000000, 0xFF800000)
 
 
 def test_e4m3_decode_spot_values_and_structure():
@@ -148,14 +168,9 @@ def test_e4m3_encode_exhaustive_near_every_midpoint():
     np.testing.assert_array_equal(oracle.e4m3_encode(v), bf.nearest_e4m3_sorted(v))
 
 
-@pytest.mark.skipif(os.environ.get("FP4Q_SLOW") != "1", reason="set FP4Q_SLOW=1")
-@pytest.mark.slow
-def test_e4m3_encode_exhaustive_range():
-    """Every fp32 pattern in [2^-11, 2^9] against a binary-search nearest-value rounding."""
-    lo, hi = 0x3A000000, 0x44000001
-    step = 1 << 23
-    for b in range(lo, hi, step):
-        v = _all_patterns(b, min(hi, b + step))
-        np.testing.assert_array_equal(oracle.e4m3_encode(v), bf.nearest_e4m3_sorted(v))
-    tiny = _all_patterns(0, 0x3A000000)[::4099]
-    np.testing.assert_array_equal(oracle.e4m3_encode(tiny), bf.nearest_e4m3_sorted(tiny))
+@pytest.mark.exhaustive
+def test_e4m3_encode_exhaustive_range(all_threads):
+    """Every non-negative finite fp32 pattern (every t the micro-scale step can
+    produce), against a nearest-value rounding by binary search in the value
+    table, evaluated at both ends of every run of equal codes."""
+    _exhaustive_runs(oracle.e4m3_encode, bf.nearest_e4m3_sorted, 0x00000000, 0x7F800000)

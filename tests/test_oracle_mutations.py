@@ -1,12 +1,14 @@
 """The oracle's pins catch plausible mistakes.
 
-Each mutant below is a copy of oracle/fp4q_oracle.c with one planted mistake of
-the kinds a from-scratch implementation could make: a wrong sign, index or
-constant, a dropped term or step, swapped operands, the wrong nibble or
-transform domain.  Each is built with the oracle's own gcc flags and the pin
-tests (tests/test_oracle_*.py, which compare the oracle with closed forms,
-brute force and properties, never with itself) run against it in a fresh
-process; every mutant must make at least one pin fail.  Every mutant stays
+Each mutant below is a copy of oracle/fp4q_oracle.c (or of the binary64 metric
+and widening in oracle/__init__.py) with one planted mistake of the kinds a
+from-scratch implementation could make: a wrong sign, index or constant, a
+dropped term or step, swapped operands, the wrong nibble, transform domain or
+summation order, the wrong norm or precision.  Each C mutant is built with the
+oracle's own gcc flags; the pin tests (tests/test_oracle_*.py, which compare
+the oracle with closed forms, brute force and properties, never with itself)
+run against it in a fresh process; every mutant must make at least one pin
+fail.  Every mutant stays
 memory-safe (no index leaves its array), so a failure is a failed pin, never a
 crash.  Runs on the CPU only."""
 import concurrent.futures
@@ -20,7 +22,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_TESTS = ["tests/test_oracle_formats.py", "tests/test_oracle_fwht.py",
              "tests/test_oracle_pipeline.py", "tests/test_oracle_requantize.py",
              "tests/test_oracle_mx.py", "tests/test_oracle_properties.py",
-             "tests/test_oracle_bf16.py"]
+             "tests/test_oracle_bf16.py", "tests/test_oracle_metrics.py"]
 
 # name -> (text in the oracle source, its replacement); the text must occur once
 MUTANTS = {
@@ -73,6 +75,8 @@ MUTANTS = {
     "re-quantise: local slice not transformed": ("if (fwht) fp4q_ref_fwht256(acc);", ""),
     "re-quantise: first peer skipped": ("for (int p = 0; p < k; ++p) {\n            decompress_block(",
                                         "for (int p = 1; p < k; ++p) {\n            decompress_block("),
+    "re-quantise: peers in reverse order": ("for (int p = 0; p < k; ++p) {\n            decompress_block(",
+                                            "for (int p = k - 1; p >= 0; --p) {\n            decompress_block("),
     # bfloat16 output option
     "bf16 round: ties away from zero": ("return (lo & 1u) ? hi : lo;", "return hi;"),
     "bf16 round: truncation": ("if (x - a < b - x) return lo;", "if (x - a < b - x || 1) return lo;"),
@@ -84,29 +88,65 @@ MUTANTS = {
 }
 
 
+# the same for oracle/__init__.py (the binary64 error metric and the widening)
+PY_MUTANTS = {
+    "rel_rmse: norm of the output in the denominator": (
+        "nx = float(np.sqrt(np.sum(x * x)))",
+        "nx = float(np.sqrt(np.sum(np.asarray(xhat, np.float64) ** 2)))"),
+    "rel_rmse: no square root": ("return float(np.sqrt(np.sum(d * d))) / nx if nx > 0 else 0.0",
+                                 "return float(np.sum(d * d)) / (nx * nx) if nx > 0 else 0.0"),
+    "rel_rmse: binary32 difference": ("d = np.asarray(xhat, np.float64) - x",
+                                      "d = (np.asarray(xhat, np.float32) - x.astype(np.float32)).astype(np.float64)"),
+    "rel_rmse: mean of per-row ratios": (
+        "return float(np.sqrt(np.sum(d * d))) / nx if nx > 0 else 0.0",
+        "return float(np.mean(np.sqrt(np.sum(np.atleast_2d(d) ** 2, axis=-1)) / "
+        "np.sqrt(np.sum(np.atleast_2d(x) ** 2, axis=-1)))) if nx > 0 else 0.0"),
+    "widen: shift by 15": ("return (np.asarray(x_bf16, np.uint16).astype(np.uint32) << 16).view(np.float32)",
+                           "return (np.asarray(x_bf16, np.uint16).astype(np.uint32) << 15).view(np.float32)"),
+}
+
+
 def _source():
     with open(os.path.join(ROOT, "oracle", "fp4q_oracle.c")) as f:
         return f.read()
 
 
+def _py_source():
+    with open(os.path.join(ROOT, "oracle", "__init__.py")) as f:
+        return f.read()
+
+
 def test_every_mutation_applies_once():
-    src = _source()
-    for name, (old, new) in MUTANTS.items():
-        assert src.count(old) == 1, "mutant %r: its text occurs %d times" % (name, src.count(old))
+    for src, table in ((_source(), MUTANTS), (_py_source(), PY_MUTANTS)):
+        for name, (old, new) in table.items():
+            assert src.count(old) == 1, "mutant %r: its text occurs %d times" % (name, src.count(old))
 
 
-def _run_pins(name, old, new, tmp):
-    """Builds the source with `old` replaced by `new` and runs the pins against
-    it in a fresh process: pytest's exit status (0 all passed, 1 a pin failed)
-    and the end of its report."""
-    tag = "".join(ch if ch.isalnum() else "_" for ch in name)
-    src_path = os.path.join(tmp, tag + ".c")
+def _run_pins(name, old, new, tmp, python=False):
+    """Builds the source with `old` replaced by `new` (python: the package's
+    __init__.py, loaded first in the test process so that every `import oracle`
+    gets the copy; the unchanged C library) and runs the pins against it in a
+    fresh process: pytest's exit status (0 all passed, 1 a pin failed) and the
+    end of its report."""
+    tag = "".join(ch if ch.isalnum() else "_" for ch in name) + ("_py" if python else "")
     lib_path = os.path.join(tmp, tag + ".so")
-    with open(src_path, "w") as f:
-        f.write(_source().replace(old, new) if old else _source())
-    subprocess.check_call(["gcc", *oracle.GCC_FLAGS, "-o", lib_path, src_path, "-lm"])
+    if python:
+        pkg = os.path.join(tmp, tag, "oracle")
+        os.makedirs(pkg)
+        with open(os.path.join(pkg, "__init__.py"), "w") as f:
+            f.write(_py_source().replace(old, new))
+        lib_path = oracle.build()
+        pre = ("import sys; sys.path.insert(0, %r); import oracle; sys.path.pop(0); "
+               "import pytest; sys.exit(pytest.main(sys.argv[1:]))" % os.path.join(tmp, tag))
+        cmd = [sys.executable, "-c", pre]
+    else:
+        src_path = os.path.join(tmp, tag + ".c")
+        with open(src_path, "w") as f:
+            f.write(_source().replace(old, new) if old else _source())
+        subprocess.check_call(["gcc", *oracle.GCC_FLAGS, "-o", lib_path, src_path, "-lm"])
+        cmd = [sys.executable, "-m", "pytest"]
     env = dict(os.environ, **{oracle.LIB_ENV: lib_path, "OMP_NUM_THREADS": "2"})
-    r = subprocess.run([sys.executable, "-m", "pytest", *PIN_TESTS, "-x", "-q", "-m", "not gpu",
+    r = subprocess.run([*cmd, *PIN_TESTS, "-x", "-q", "-m", "not gpu and not exhaustive",
                         "-p", "no:cacheprovider"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return r.returncode, r.stdout[-1500:]
@@ -117,6 +157,8 @@ def test_pins_catch_every_mutant(tmp_path):
         control = pool.submit(_run_pins, "unchanged", "", "", str(tmp_path))
         futs = {name: pool.submit(_run_pins, name, old, new, str(tmp_path))
                 for name, (old, new) in MUTANTS.items()}
+        futs.update({name: pool.submit(_run_pins, name, old, new, str(tmp_path), True)
+                     for name, (old, new) in PY_MUTANTS.items()})
         # the unchanged source, built and loaded the same way, passes every pin
         rc, report = control.result()
         assert rc == 0, "the unchanged oracle fails its pins in this harness:\n" + report
