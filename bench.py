@@ -266,6 +266,66 @@ def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
     return "\n".join(out)
 
 
+SIMDS, XCDS = 1024, 8   # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
+PMC_KERNELS = ("compress_kernel<true>", "compress_kernel<false>", "decompress_kernel<true, false>",
+               "decompress_kernel<true, true>", "accumulate_kernel<true, false>",
+               "requantize_kernel<false, true>", "requantize_kernel<true, true>")
+
+
+def summarize_pmc(dirs) -> str:
+    """Per-kernel counter summary (markdown) from rocprofv3 --pmc runs (one
+    directory per pass): for each headline and receiver kernel at its largest
+    grid, the median over its dispatches of every counter collected, then the
+    per-wavefront instruction mix and the shares of wavefront time."""
+    vals, dur, grid_of = {}, {}, {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel<[^>]*>|accumulate_kernel<[^>]*>|"
+                              r"requantize_kernel<[^>]*>)", r["Kernel_Name"])
+                if not m or m.group(1) not in PMC_KERNELS:
+                    continue
+                k, g = m.group(1), int(r["Grid_Size"])
+                if g < grid_of.get(k, 0):
+                    continue
+                if g > grid_of.get(k, 0):
+                    grid_of[k] = g
+                    vals[k], dur[k] = {}, []
+                vals[k].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    med = {k: {c: float(np.median(v)) for c, v in vals[k].items()} for k in vals}
+    names = sorted({c for k in med for c in med[k]})
+    out = ["| kernel | grid | us (under counters) | " + " | ".join(names) + " |",
+           "|---|---|---|" + "---|" * len(names)]
+    for k in PMC_KERNELS:
+        if k in med:
+            out.append("| %s | %d | %.1f | " % (k, grid_of[k], float(np.median(dur[k]))) +
+                       " | ".join("%.0f" % med[k].get(c, float("nan")) for c in names) + " |")
+    out += ["", "Derived, per wavefront (instructions) and as shares of the wavefronts' resident "
+            "time SQ_WAVE_CYCLES (all in the same quad-cycle units); SIMD VALU busy = "
+            "SQ_ACTIVE_INST_VALU x 4 cycles / %d SIMDs / (GRBM_GUI_ACTIVE / %d XCDs); clock = "
+            "GRBM_GUI_ACTIVE / %d / duration:" % (SIMDS, XCDS, XCDS), "",
+            "| kernel | waves | VALU | SALU | LDS | VMEM rd | VMEM wr | VALU active / wave time | "
+            "any inst active / wave time | waiting / wave time | SIMD VALU busy | clock GHz |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in PMC_KERNELS:
+        c = med.get(k)
+        if not c or not c.get("SQ_WAVES"):
+            continue
+        w = c["SQ_WAVES"]
+        per = lambda n: ("%.0f" % (c[n] / w)) if n in c else "-"
+        frac = lambda n: ("%.3f" % (c[n] / c["SQ_WAVE_CYCLES"])) if n in c and c.get("SQ_WAVE_CYCLES") else "-"
+        gui = c.get("GRBM_GUI_ACTIVE")
+        busy = ("%.3f" % (c["SQ_ACTIVE_INST_VALU"] * 4 / SIMDS / (gui / XCDS))) \
+            if gui and "SQ_ACTIVE_INST_VALU" in c else "-"
+        clock = ("%.2f" % (gui / XCDS / (float(np.median(dur[k])) * 1e3))) if gui else "-"
+        out.append("| %s | %.0f | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            k, w, per("SQ_INSTS_VALU"), per("SQ_INSTS_SALU"), per("SQ_INSTS_LDS"), per("SQ_INSTS_VMEM_RD"),
+            per("SQ_INSTS_VMEM_WR"), frac("SQ_ACTIVE_INST_VALU"), frac("SQ_ACTIVE_INST_ANY"),
+            frac("SQ_WAIT_INST_ANY"), busy, clock))
+    return "\n".join(out)
+
+
 def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
     """The receiver's kernels on the reduce workload (k = 8 peers of 4096 x 11008,
     N(0, 1e-3)): fp4q_decompress_accumulate (fp32 out), fp4q_reduce_requantize, and
@@ -749,11 +809,17 @@ def main():
     ap.add_argument("--timed-steps", type=int, default=0,
                     help="with --summarize-trace: the traced run's --steps, to report its timed "
                          "region's launches of the headline kernels on their own")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="PMC_DIR",
+                    help="print the per-kernel summary of rocprofv3 --pmc runs (one directory per "
+                         "pass) and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the kernel durations of a rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.timed_steps))
