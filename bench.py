@@ -140,11 +140,11 @@ def measured_traffic(path: str = None):
 
 
 def _short(kernel_name: str) -> str:
-    if "requantize_kernel<true" in kernel_name:
+    if "requantize_kernel<" in kernel_name:          # with the rank's own slice
         return "requantize_local"
-    for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate", "requantize"):
+    for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate", "requantize_narrow"):
         if fam + "_kernel" in kernel_name:
-            return fam
+            return fam.replace("_narrow", "")
     if "copyBuffer" in kernel_name:
         return "copy"
     return kernel_name.split("(")[0][:40]
@@ -237,8 +237,8 @@ def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))   # dispatch order
     groups = {}
     for r in rows:
-        m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel(?:<[^>]*>)?)",
-                      r["Kernel_Name"])
+        m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel<[^>]*>|"
+                      r"requantize_narrow_kernel)", r["Kernel_Name"])
         if not m:
             continue
         grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
@@ -269,7 +269,7 @@ def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
 SIMDS, XCDS = 1024, 8   # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
 PMC_KERNELS = ("compress_kernel<true>", "compress_kernel<false>", "decompress_kernel<true, false>",
                "decompress_kernel<true, true>", "accumulate_kernel<true, false>",
-               "requantize_kernel<false, true>", "requantize_kernel<true, true>")
+               "requantize_narrow_kernel", "requantize_kernel<true>")
 
 
 def summarize_pmc(dirs) -> str:
@@ -282,7 +282,7 @@ def summarize_pmc(dirs) -> str:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel<[^>]*>|accumulate_kernel<[^>]*>|"
-                              r"requantize_kernel<[^>]*>)", r["Kernel_Name"])
+                              r"requantize_kernel<[^>]*>|requantize_narrow_kernel)", r["Kernel_Name"])
                 if not m or m.group(1) not in PMC_KERNELS:
                     continue
                 k, g = m.group(1), int(r["Grid_Size"])

@@ -151,11 +151,11 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
 constexpr int kStorePolicy = 16;  // sc1
 struct TileStore {
     __amdgpu_buffer_rsrc_t r;
-    // bytes_per_block of the array, for the tile's blocks [tile, tile + 16) that exist
+    // bytes_per_block of the array, for the tile's blocks [tile, tile + tile_blocks) that exist
     __device__ __forceinline__ TileStore(void *base, int64_t tile, int64_t nblocks,
-                                         int bytes_per_block) {
+                                         int bytes_per_block, int tile_blocks = kTileBlocks) {
         const int64_t left = nblocks - tile;
-        const int64_t nvalid = left < 0 ? 0 : left < kTileBlocks ? left : kTileBlocks;
+        const int64_t nvalid = left < 0 ? 0 : left < tile_blocks ? left : tile_blocks;
         r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(base) + tile * bytes_per_block, 0,
                                               static_cast<int>(nvalid * bytes_per_block), 0x00020000);
     }
@@ -362,6 +362,61 @@ __device__ __forceinline__ void compress_transform(const Lane &L, uint4 *__restr
 //   s  = max|y| / 2688 over the block;  t_k = max|y|_k / (6 s), clamped to 448;
 //   mw = the four E4M3 micro-scales (byte k);  C = eight dwords of packed codes
 //        (dword w covers registers 8 w .. 8 w + 7, low nibble first).
+// The dual scales of a block from its largest |y|, A (already reduced over the
+// block's lanes), and the lane's K group maxima a[k] (K even):
+//   s = A / 2688;  t_k = a_k / (6 s), clamped to 448;  mw = the K E4M3
+//   micro-scales (byte k);  inv[k] = 1 / (s * E4M3(m_k)), 0 for a zero scale.
+template <int K>
+__device__ __forceinline__ void dual_scales(float A, const float (&a)[K], float &s, float (&t)[K],
+                                            unsigned &mw, float (&inv)[K]) {
+    static_assert(K == 2 || K == 4, "two or four micro-groups per lane");
+    const auto pack = [&]() {
+        mw = e4m3_pair<false>(0u, t[0], t[1]);
+        if constexpr (K == 4) mw = e4m3_pair<true>(mw, t[2], t[3]);
+    };
+    if (A >= 0x1p-80f) {
+        s = coarse_scale(A);
+        const float d6 = 6.0f * s;
+        const float y = rcp_rn(d6);
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = fminf(div_rn(a[k], d6, y), kE4M3Max);
+        pack();
+        static_for<K>([&](auto k) {
+            const float S = s * e4m3_value<decltype(k)::value>(mw);
+            inv[k] = (S == 0.0f) ? 0.0f : rcp_rn(S);
+        });
+    } else {  // tiny or zero block: IEEE division throughout
+        s = A / fp4q_num::kScaleDivisor;
+        const float d6 = 6.0f * s;
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, kE4M3Max) : 0.0f;
+        pack();
+        static_for<K>([&](auto k) {
+            const float S = s * e4m3_value<decltype(k)::value>(mw);
+            inv[k] = fminf((S == 0.0f) ? 0.0f : 1.0f / S, FLT_MAX);
+        });
+    }
+}
+
+// E2M1 codes of the lane's N registers, 16 per micro-group k (scale inv[k]):
+// dword w of C covers registers 8 w .. 8 w + 7, low nibble first.
+template <int N>
+__device__ __forceinline__ void quantize_codes(const float (&R)[N], const float (&inv)[N / 16],
+                                               unsigned (&C)[N / 8]) {
+#pragma unroll
+    for (int w = 0; w < N / 8; ++w) {
+        const float r = inv[w >> 1];
+        // the four conversions write all four bytes of c; starting from a
+        // register that dies here (instead of 0) saves a move per dword
+        unsigned c = as_u(R[8 * w]);
+        static_for<4>([&](auto sel) {
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            c = e2m1_pair<decltype(sel)::value>(c, R[j] * r, R[j + 1] * r);
+        });
+        C[w] = c;
+    }
+}
+
 template <bool kScaled>
 __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, float (&t)[4],
                                                 unsigned &mw, unsigned (&C)[8]) {
@@ -374,46 +429,13 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
         a[k] = kScaled ? m * 0.0625f : m;
     }
     const float A = block_lane_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
-
     float inv[4];
-    if (A >= 0x1p-80f) {
-        s = coarse_scale(A);
-        const float d6 = 6.0f * s;
-        const float y = rcp_rn(d6);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = fminf(div_rn(a[k], d6, y), kE4M3Max);
-        mw = e4m3_pair<true>(e4m3_pair<false>(0u, t[0], t[1]), t[2], t[3]);
-        static_for<4>([&](auto k) {
-            const float S = s * e4m3_value<decltype(k)::value>(mw);
-            inv[k] = (S == 0.0f) ? 0.0f : rcp_rn(S);
-        });
-    } else {  // tiny or zero block: IEEE division throughout
-        s = A / fp4q_num::kScaleDivisor;
-        const float d6 = 6.0f * s;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = (s != 0.0f) ? fminf(a[k] / d6, kE4M3Max) : 0.0f;
-        mw = e4m3_pair<true>(e4m3_pair<false>(0u, t[0], t[1]), t[2], t[3]);
-        static_for<4>([&](auto k) {
-            const float S = s * e4m3_value<decltype(k)::value>(mw);
-            inv[k] = fminf((S == 0.0f) ? 0.0f : 1.0f / S, FLT_MAX);
-        });
-    }
+    dual_scales<4>(A, a, s, t, mw, inv);
     if constexpr (kScaled) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) inv[k] *= 0.0625f;  // exact: the folded 1/16
     }
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        const float r = inv[w >> 1];
-        // the four conversions write all four bytes of c; starting from a
-        // register that dies here (instead of 0) saves a move per dword
-        unsigned c = as_u(R[8 * w]);
-        static_for<4>([&](auto sel) {
-            const int j = 8 * w + 2 * decltype(sel)::value;
-            c = e2m1_pair<decltype(sel)::value>(c, R[j] * r, R[j + 1] * r);
-        });
-        C[w] = c;
-    }
+    quantize_codes<64>(R, inv, C);
 }
 
 // Codes of a tile through LDS (8 chunks per block, stride 9); the tile's 2 KiB
@@ -811,9 +833,10 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
 // summed where they live, in the transform domain (rounded products added in
 // peer order), and the sum is quantised again with the compress steps -- no
 // inverse transform is needed, since decompressing, summing and compressing
-// would apply the self-inverse H / 16 twice.  The accumulator starts at +0, or
-// (kLocal) at the rank's own uncompressed part of the slice, transformed as
-// compress transforms its input.
+// would apply the self-inverse H / 16 twice.  With the rank's own uncompressed
+// part of the slice (this kernel), the accumulator starts at that part,
+// transformed as compress transforms its input; without one it starts at +0
+// (requantize_narrow_kernel below).
 // Register j of quarter q holds element 32 q + 128 (j >> 5) + (j & 31), so
 // register group k = j >> 4 is micro-group (k & 1) + 2 q + 8 (k >> 1), and code
 // dwords 0-3 / 4-7 are the block's 16-byte chunks q / q + 4.
@@ -842,23 +865,17 @@ __device__ __forceinline__ void local_transform(float (&R)[64]) {
     }
 }
 
-template <bool kLocal, bool kFwht>
+template <bool kFwht>
 __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     Peers peers, int k, const uint4 *__restrict__ local, int64_t nblocks,
     uint4 *__restrict__ codes, unsigned short *__restrict__ micro, float *__restrict__ block) {
-    constexpr int kChunks = kLocal ? kStageChunks : 144;
-    __shared__ uint4 lds_all[kReceiverWaves * kChunks];
+    __shared__ uint4 lds_all[kReceiverWaves * kStageChunks];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
-    uint4 *lds = lds_all + (threadIdx.x / kWave) * kChunks;
+    uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
     float R[64];
-    if constexpr (kLocal) {
-        load_widen<false>(L, local, nblocks, lds, R);
-        local_transform<kFwht>(R);
-        wave_lds_sync();  // every lane has read its input chunks
-    } else {
-#pragma unroll
-        for (int j = 0; j < 64; ++j) R[j] = 0.0f;
-    }
+    load_widen<false>(L, local, nblocks, lds, R);
+    local_transform<kFwht>(R);
+    wave_lds_sync();  // every lane has read its input chunks
     sum_peers<kAdd>(L, nblocks, peers, k, lds, R);
 
     float s, t[4];
@@ -870,6 +887,114 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
         m.b16(16 * L.p + 2 * L.q, (unsigned short)(mw & 0xFFFFu));      // groups 2q, 2q + 1
         m.b16(16 * L.p + 8 + 2 * L.q, (unsigned short)(mw >> 16));      // groups 2q + 8, 2q + 9
         if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, as_u(s));
+    }
+}
+
+// Without a local slice the re-quantisation applies no transform, so nothing
+// ties a block's elements to one lane's registers across the whole block.  This
+// kernel uses a narrow layout instead: a wavefront handles kNarrowBlocks = 8
+// blocks and lane l works on block p = l >> 3 and its eighth e = l & 7, the 32
+// elements [32 e, 32 e + 32) (micro-groups 2 e and 2 e + 1).  Every peer's codes
+// for the tile then arrive in one contiguous 1 KiB load (16 bytes per lane),
+// the new codes leave the same way, and micro-scales move as one 2-byte pair
+// per lane: no LDS, 32 accumulator registers instead of 64, twice the resident
+// wavefronts.  The block maximum is reduced over the block's eight lanes.
+constexpr int kNarrowBlocks = 8;
+
+struct NarrowLane {
+    int lane, p, e;
+    int64_t tile, b, bl;
+    bool valid;
+};
+
+template <int kWaves>
+__device__ __forceinline__ NarrowLane narrow_map(int64_t nblocks) {
+    NarrowLane L;
+    L.lane = threadIdx.x & (kWave - 1);
+    const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    L.tile = ((int64_t)blockIdx.x * kWaves + wave_in_wg) * kNarrowBlocks;
+    L.p = L.lane >> 3;
+    L.e = L.lane & 7;
+    L.b = L.tile + L.p;
+    L.valid = L.b < nblocks;
+    L.bl = L.valid ? L.b : nblocks - 1;  // lanes past the end compute on the last block, never store
+    return L;
+}
+
+// Maximum of v over the eight lanes of a block (lane bits 0-2), by swizzles
+// within groups of 32 lanes (xor 1, 2, 4).
+__device__ __forceinline__ float octet_max(float v) {
+    v = fmaxf(v, as_f(__builtin_amdgcn_ds_swizzle(as_u(v), 0x041F)));
+    v = fmaxf(v, as_f(__builtin_amdgcn_ds_swizzle(as_u(v), 0x081F)));
+    return fmaxf(v, as_f(__builtin_amdgcn_ds_swizzle(as_u(v), 0x101F)));
+}
+
+struct NarrowPayload {
+    uint4 c;     // 32 codes: elements 32 e .. 32 e + 31
+    unsigned m;  // micro-scale bytes 2 e, 2 e + 1 in the low half
+    float s;
+};
+
+__device__ __forceinline__ NarrowPayload load_narrow(const NarrowLane &L, const uint4 *__restrict__ codes,
+                                                     const uint4 *__restrict__ micro,
+                                                     const float *__restrict__ block) {
+    NarrowPayload P;
+    P.c = load_nt(codes + L.bl * 8 + L.e);
+    P.m = reinterpret_cast<const unsigned short *>(micro)[L.bl * 8 + L.e];
+    P.s = block[L.bl];
+    return P;
+}
+
+// R[j] = R[j] + E2M1(code j) * S_g: a rounded product, then a rounded sum (the
+// order the re-quantisation defines).
+__device__ __forceinline__ void dequant_add_narrow(const NarrowPayload &P, float (&R)[32]) {
+    const unsigned C[4] = {P.c.x, P.c.y, P.c.z, P.c.w};
+    const float S[2] = {P.s * e4m3_value<0>(P.m), P.s * e4m3_value<1>(P.m)};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float Sg = S[w >> 1];
+        static_for<4>([&](auto sel) {
+            const auto f = e2m1_values<decltype(sel)::value>(C[w]);
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            const float p0 = f[0] * Sg, p1 = f[1] * Sg;  // built without contraction
+            R[j] = R[j] + p0;
+            R[j + 1] = R[j + 1] + p1;
+        });
+    }
+}
+
+__global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_narrow_kernel(
+    Peers peers, int k, int64_t nblocks, uint4 *__restrict__ codes, unsigned short *__restrict__ micro,
+    float *__restrict__ block) {
+    const NarrowLane L = narrow_map<kReceiverWaves>(nblocks);
+    float R[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) R[j] = 0.0f;
+    // one peer's loads in flight while the previous one is added (k is wave-uniform)
+    NarrowPayload P = load_narrow(L, peers.codes[0], peers.micro[0], peers.block[0]);
+    for (int p = 0; p < k; ++p) {
+        const NarrowPayload cur = P;
+        if (p + 1 < k) P = load_narrow(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
+        dequant_add_narrow(cur, R);
+    }
+
+    float a[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(R[16 * g + i]));
+        a[g] = m;
+    }
+    const float A = octet_max(fmaxf(a[0], a[1]));
+    float s, t[2], inv[2];
+    unsigned mw, C[4];
+    dual_scales<2>(A, a, s, t, mw, inv);
+    quantize_codes<32>(R, inv, C);
+    if (L.valid) {
+        TileStore(codes, L.tile, nblocks, 128, kNarrowBlocks).b128(16 * L.lane, make_uint4(C[0], C[1], C[2], C[3]));
+        TileStore(micro, L.tile, nblocks, 16, kNarrowBlocks).b16(16 * L.p + 2 * L.e, (unsigned short)(mw & 0xFFFFu));
+        if (L.e == 0) TileStore(block, L.tile, nblocks, 4, kNarrowBlocks).b32(4 * L.p, as_u(s));
     }
 }
 
@@ -1010,8 +1135,9 @@ int check_shape(int64_t rows, int64_t row_len, int64_t *n, int64_t *nb) {
     return FP4Q_OK;
 }
 
-int launch(const void *fn, int64_t nb, int waves, void **args, void *stream) {
-    const int64_t per_wg = (int64_t)kTileBlocks * waves;
+int launch(const void *fn, int64_t nb, int waves, void **args, void *stream,
+           int tile_blocks = kTileBlocks) {
+    const int64_t per_wg = (int64_t)tile_blocks * waves;
     const dim3 grid((unsigned)((nb + per_wg - 1) / per_wg)), threads(kWave * waves);
     const hipError_t e = hipLaunchKernel(fn, grid, threads, args, 0, (hipStream_t)stream);
     return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_LAUNCH;
@@ -1171,11 +1297,14 @@ int fp4q_reduce_requantize_ex(int k, const uint8_t *const *codes,
         peers.micro[p] = reinterpret_cast<const uint4 *>(micro_scales[p]);
         peers.block[p] = block_scales[p];
     }
+    if (!local_bf16) {  // no transform anywhere: the narrow layout
+        void *args[] = {&peers, &k, &nb, &out_codes, &out_micro, &out_block};
+        return launch((const void *)&requantize_narrow_kernel, nb, kReceiverWaves, args, stream,
+                      kNarrowBlocks);
+    }
     void *args[] = {&peers, &k, &local_bf16, &nb, &out_codes, &out_micro, &out_block};
     const bool fw = !(flags & FP4Q_FLAG_NO_FWHT);
-    const void *fn = !local_bf16 ? (const void *)&requantize_kernel<false, true>
-                     : fw        ? (const void *)&requantize_kernel<true, true>
-                                 : (const void *)&requantize_kernel<true, false>;
+    const void *fn = fw ? (const void *)&requantize_kernel<true> : (const void *)&requantize_kernel<false>;
     return launch(fn, nb, kReceiverWaves, args, stream);
 }
 
