@@ -140,6 +140,8 @@ def measured_traffic(path: str = None):
 
 
 def _short(kernel_name: str) -> str:
+    if "twin_" in kernel_name:                       # the traffic twins of the ceilings leg
+        return "twin"
     if "requantize_kernel<" in kernel_name:          # with the rank's own slice
         return "requantize_local"
     for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate", "requantize_narrow"):
@@ -459,6 +461,90 @@ def variant_timing(fp4q, torch, X, P, Y, iters: int = 40):
     for s in range(S):
         fp4q.fp4q_compress(X[s], *P[s])
     torch.cuda.synchronize()
+    return res
+
+
+TWINS_LIB = os.path.join(ROOT, "tests", "hip", "libfp4q_twins.so")
+
+
+def ceilings(fp4q, inputs, torch, dev, X, P, Y, iters: int = 40):
+    """Compute-free traffic twins of the kernels (tests/hip/fp4q_twins.hip: the
+    same launch shape and the same memory instructions, calling the kernels' own
+    load and store functions, with the arithmetic left out), timed like the
+    variants on the same buffers: what each kernel's exact traffic pattern costs
+    the memory system.  Plus plain read and write streams of 512 MiB (1 KiB per
+    instruction, the library's load and store policies).  None if the twins
+    library has not been built."""
+    if not os.path.exists(TWINS_LIB):
+        log("ceilings: %s not built, skipped" % TWINS_LIB)
+        return None
+    import ctypes
+    L = ctypes.CDLL(TWINS_LIB)
+    Pp, I64 = ctypes.c_void_p, ctypes.c_int64
+    L.twin_compress.argtypes = [Pp, I64, I64, Pp, Pp, Pp, Pp]
+    L.twin_decompress.argtypes = [Pp, Pp, Pp, I64, I64, Pp, ctypes.c_int, Pp]
+    L.twin_accumulate.argtypes = [ctypes.c_int, Pp, Pp, Pp, I64, I64, Pp, Pp]
+    L.twin_read.argtypes = [Pp, I64, Pp, Pp]
+    L.twin_write.argtypes = [Pp, I64, Pp]
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows, Lr = X[0].shape
+    n = rows * Lr
+    S = len(X)
+    ab = algorithmic_bytes(n)
+    k, rr, rl = REDUCE_K, 4096, 11008
+    pays = [fp4q.fp4q_compress(torch.from_numpy(q.view(np.int16)).to(dev)) for q in reduce_peers(inputs)]
+    PA = ctypes.c_void_p * k
+    cs, ms, bs = (PA(*[ptr(q[i]) for q in pays]) for i in range(3))
+    racc = torch.empty((rr, rl), dtype=torch.float32, device=dev)
+    nbig = 512 << 20
+    big = [torch.empty(nbig, dtype=torch.uint8, device=dev) for _ in range(2)]
+    sink = torch.empty(nbig // 1024, dtype=torch.uint8, device=dev)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("twin launch failed: %d" % rc)
+
+    cases = (
+        ("compress", lambda i: ok(L.twin_compress(ptr(X[i % S]), rows, Lr, *[ptr(t) for t in P[i % S]], stream())),
+         ab["compress"]),
+        ("decompress", lambda i: ok(L.twin_decompress(*[ptr(t) for t in P[i % S]], rows, Lr, ptr(Y[i % S]), 0,
+                                                      stream())), ab["decompress"]),
+        ("decompress_bf16_out", lambda i: ok(L.twin_decompress(*[ptr(t) for t in P[i % S]], rows, Lr,
+                                                               ptr(Y[i % S]), 1, stream())),
+         ab["decompress"] - 2 * n),
+        ("accumulate_k8", lambda i: ok(L.twin_accumulate(k, cs, ms, bs, rr, rl, ptr(racc), stream())),
+         _receiver_bytes()["accumulate"]),
+        # written first: reads of never-written pages were served at an impossible 22 TB/s
+        ("write_512MiB", lambda i: ok(L.twin_write(ptr(big[i % 2]), nbig, stream())), nbig),
+        ("read_512MiB", lambda i: ok(L.twin_read(ptr(big[i % 2]), nbig, ptr(sink), stream())), nbig),
+    )
+    res = {}
+    for name, fn, nbytes in cases:
+        for i in range(6):
+            fn(i)
+        torch.cuda.synchronize()
+        for i in range(16):
+            fn(i)
+        ev = [(TimingEvent(), TimingEvent()) for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        med = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+        gbps = nbytes / med / 1e9
+        res[name] = {"median_us": round(med * 1e6, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
+                     "frac": round(gbps / PEAK_GBPS, 4)}
+        log("ceiling %-14s median %7.1f us  %7.1f GB/s  %.1f%% of HBM peak" % (
+            name, med * 1e6, gbps, 100 * gbps / PEAK_GBPS))
+    del pays, racc, big, sink
+    # the twins wrote the step's payloads and outputs: restore the payloads
+    for s_ in range(S):
+        fp4q.fp4q_compress(X[s_], *P[s_])
+    torch.cuda.synchronize()
+    res["what"] = ("compute-free kernels with each kernel's launch shape and memory instructions "
+                   "(tests/hip/fp4q_twins.hip); read/write: plain 512 MiB streams")
     return res
 
 
@@ -802,6 +888,8 @@ def main():
     ap.add_argument("--no-tradeoff", action="store_true",
                     help="skip the throughput and error report with and without the transform "
                          "on the 2048x4096 and 8192x4096 workloads (cache-resident)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip timing the compute-free traffic twins of the kernels")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain %d-byte device copy (counter scale reference)" % COPY_REF_BYTES)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -873,6 +961,8 @@ def main():
             result["receiver"] = receiver_timing(fp4q, inputs, torch, dev)
         if not args.no_tradeoff:
             result["tradeoff"] = fwht_tradeoff(fp4q, inputs, torch, dev)
+        if not args.no_ceilings:
+            result["ceilings"] = ceilings(fp4q, inputs, torch, dev, X, P, Y)
         # the copy ceiling's 512 MiB copies would join the counter-scale reference's
         # 256 MiB copies in a --copy-reference run (the summary takes the largest copies)
         if not args.copy_reference:

@@ -130,3 +130,15 @@ def test_traffic_is_read_only_for_the_current_kernel_source(tmp_path, monkeypatc
     f.write_text("text\ntraffic: source=0123456789abcdef compress=11 decompress=22\n")
     assert bench.measured_traffic(str(f)) is None
     assert bench.measured_traffic(str(tmp_path / "missing.md")) is None
+
+
+def test_kernel_families():
+    """Counter and trace summaries group dispatches by kernel family; the traffic
+    twins of the ceilings leg never count as the kernels they mirror."""
+    ns = "void (anonymous namespace)::"
+    assert bench._short(ns + "decompress_kernel<true, false>(x)") == "decompress"
+    assert bench._short(ns + "twin_decompress_kernel(x)") == "twin"
+    assert bench._short(ns + "twin_compress_kernel(x)") == "twin"
+    assert bench._short(ns + "requantize_narrow_kernel(x)") == "requantize"
+    assert bench._short(ns + "requantize_kernel<true>(x)") == "requantize_local"
+    assert bench._short(ns + "compress_mx_kernel<true>(x)") == "compress_mx"
