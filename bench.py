@@ -144,7 +144,8 @@ def _short(kernel_name: str) -> str:
         return "twin"
     if "requantize_kernel<" in kernel_name:          # with the rank's own slice
         return "requantize_local"
-    for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate", "requantize_narrow"):
+    for fam in ("decompress_mx", "compress_mx", "decompress", "compress", "accumulate_narrow", "accumulate",
+                "requantize_narrow"):
         if fam + "_kernel" in kernel_name:
             return fam.replace("_narrow", "")
     if "copyBuffer" in kernel_name:
@@ -227,6 +228,11 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> str:
     return "\n".join(out)
 
 
+# The library's kernels as named in a profiler's records (templates with their arguments).
+KERNEL_NAME = re.compile(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate(?:_narrow)?_kernel<[^>]*>|"
+                         r"requantize_kernel<[^>]*>|requantize_narrow_kernel)")
+
+
 def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
     """Per-dispatch kernel durations from a rocprofv3 --kernel-trace run (markdown):
     each of this library's kernel instantiations at its largest grid.  With
@@ -239,8 +245,7 @@ def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))   # dispatch order
     groups = {}
     for r in rows:
-        m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel(?:<[^>]*>)?|accumulate_kernel<[^>]*>|requantize_kernel<[^>]*>|"
-                      r"requantize_narrow_kernel)", r["Kernel_Name"])
+        m = KERNEL_NAME.search(r["Kernel_Name"])
         if not m:
             continue
         grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
@@ -270,7 +275,7 @@ def summarize_trace(trace_dir: str, timed_steps: int = 0) -> str:
 
 SIMDS, XCDS = 1024, 8   # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
 PMC_KERNELS = ("compress_kernel<true>", "compress_kernel<false>", "decompress_kernel<true, false>",
-               "decompress_kernel<true, true>", "accumulate_kernel<true, false>",
+               "decompress_kernel<true, true>", "accumulate_narrow_kernel<true, false>",
                "requantize_narrow_kernel", "requantize_kernel<true>")
 
 
@@ -283,8 +288,7 @@ def summarize_pmc(dirs) -> str:
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                m = re.search(r"\b((?:de)?compress(?:_mx)?_kernel<[^>]*>|accumulate_kernel<[^>]*>|"
-                              r"requantize_kernel<[^>]*>|requantize_narrow_kernel)", r["Kernel_Name"])
+                m = KERNEL_NAME.search(r["Kernel_Name"])
                 if not m or m.group(1) not in PMC_KERNELS:
                     continue
                 k, g = m.group(1), int(r["Grid_Size"])
@@ -494,9 +498,11 @@ def ceilings(fp4q, inputs, torch, dev, X, P, Y, iters: int = 40):
     ab = algorithmic_bytes(n)
     k, rr, rl = REDUCE_K, 4096, 11008
     pays = [fp4q.fp4q_compress(torch.from_numpy(q.view(np.int16)).to(dev)) for q in reduce_peers(inputs)]
+    # three rotating copies of the peers and outputs, as the receiver leg times the kernels
+    psets = [pays] + [[tuple(t.clone() for t in q) for q in pays] for _ in range(2)]
     PA = ctypes.c_void_p * k
-    cs, ms, bs = (PA(*[ptr(q[i]) for q in pays]) for i in range(3))
-    racc = torch.empty((rr, rl), dtype=torch.float32, device=dev)
+    ptrs = [tuple(PA(*[ptr(q[i]) for q in ps]) for i in range(3)) for ps in psets]
+    raccs = [torch.empty((rr, rl), dtype=torch.float32, device=dev) for _ in range(3)]
     nbig = 512 << 20
     big = [torch.empty(nbig, dtype=torch.uint8, device=dev) for _ in range(2)]
     sink = torch.empty(nbig // 1024, dtype=torch.uint8, device=dev)
@@ -513,7 +519,7 @@ def ceilings(fp4q, inputs, torch, dev, X, P, Y, iters: int = 40):
         ("decompress_bf16_out", lambda i: ok(L.twin_decompress(*[ptr(t) for t in P[i % S]], rows, Lr,
                                                                ptr(Y[i % S]), 1, stream())),
          ab["decompress"] - 2 * n),
-        ("accumulate_k8", lambda i: ok(L.twin_accumulate(k, cs, ms, bs, rr, rl, ptr(racc), stream())),
+        ("accumulate_k8", lambda i: ok(L.twin_accumulate(k, *ptrs[i % 3], rr, rl, ptr(raccs[i % 3]), stream())),
          _receiver_bytes()["accumulate"]),
         # written first: reads of never-written pages were served at an impossible 22 TB/s
         ("write_512MiB", lambda i: ok(L.twin_write(ptr(big[i % 2]), nbig, stream())), nbig),
@@ -538,7 +544,7 @@ def ceilings(fp4q, inputs, torch, dev, X, P, Y, iters: int = 40):
                      "frac": round(gbps / PEAK_GBPS, 4)}
         log("ceiling %-14s median %7.1f us  %7.1f GB/s  %.1f%% of HBM peak" % (
             name, med * 1e6, gbps, 100 * gbps / PEAK_GBPS))
-    del pays, racc, big, sink
+    del pays, psets, raccs, big, sink
     # the twins wrote the step's payloads and outputs: restore the payloads
     for s_ in range(S):
         fp4q.fp4q_compress(X[s_], *P[s_])

@@ -36,6 +36,12 @@
 // private to each wavefront.  No MFMA: the work is streaming and the transform
 // is butterflies.
 //
+// The k-peer kernels whose time is their per-peer arithmetic use a narrow
+// layout instead (8 blocks per wavefront, 32 elements per lane: each peer's
+// codes in one contiguous 1 KiB load, half the registers, twice the resident
+// wavefronts): the receiver reduce, and the re-quantisation without a local
+// slice, which needs no transform at all.
+//
 // Numerics follow the method's fp32 operation order exactly (built with
 // -ffp-contract=off, IEEE division, fp32 denormals kept):
 //   * the transform runs on unscaled values z = 16 y; the 1/16 is folded into
@@ -612,9 +618,9 @@ __device__ __forceinline__ void redeal_codes(const Lane &L, uint4 *__restrict__ 
 }
 
 // Registers j = 0..63 get E2M1(code) * S_g (kSet), or the product is added to
-// them with one fused multiply-add (kFma) or as a rounded product and a rounded
-// sum (kAdd, the order the re-quantisation defines).
-enum DequantMode { kSet, kFma, kAdd };
+// them as a rounded product and a rounded sum (kAdd, the order the
+// re-quantisation defines).
+enum DequantMode { kSet, kAdd };
 template <DequantMode kMode>
 __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64], float dscale = 1.0f) {
     const unsigned C[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
@@ -626,10 +632,7 @@ __device__ __forceinline__ void dequant(const PayloadRegs &P, float (&R)[64], fl
         static_for<4>([&](auto sel) {
             const auto f = e2m1_values<decltype(sel)::value>(C[w], dscale);
             const int j = 8 * w + 2 * decltype(sel)::value;
-            if constexpr (kMode == kFma) {
-                R[j] = fmaf(f[0], Sg, R[j]);
-                R[j + 1] = fmaf(f[1], Sg, R[j + 1]);
-            } else if constexpr (kMode == kAdd) {
+            if constexpr (kMode == kAdd) {
                 const float p0 = f[0] * Sg, p1 = f[1] * Sg;  // built without contraction
                 R[j] = R[j] + p0;
                 R[j + 1] = R[j + 1] + p1;
@@ -778,10 +781,11 @@ struct Peers {
     const float *block[FP4Q_MAX_PEERS];
 };
 
-// Sum of k payloads into R (mode kFma or kAdd) with kInFlight payloads' loads
-// outstanding: the loads of peer p + kInFlight are issued as soon as peer p has
-// been dequantised.  Codes are loaded contiguously and re-dealt through the
-// wavefront's LDS region lds (free during the sum, at least 144 chunks).  k is wave-uniform, so every branch here is uniform.  One
+// Sum of k payloads into R (as rounded products and rounded sums, kAdd) with
+// kInFlight payloads' loads outstanding: the loads of peer p + kInFlight are
+// issued as soon as peer p has been dequantised.  Codes are loaded contiguously
+// and re-dealt through the wavefront's LDS region lds (free during the sum, at
+// least 144 chunks).  k is wave-uniform, so every branch here is uniform.  One
 // payload in flight measured best: every further buffer costs 12 registers, and
 // the resident wavefronts those registers would allow hide more latency.
 #ifndef FP4Q_PEERS_IN_FLIGHT
@@ -808,23 +812,6 @@ __device__ __forceinline__ void sum_peers(const Lane &L, int64_t nblocks, const 
             }
         }
     }
-}
-
-
-// Sum in the transform domain (the transform is linear), then one inverse
-// transform for all peers.
-template <bool kFwht, bool kBf16>
-__global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_kernel(
-    Peers peers, int k, int64_t nblocks, void *__restrict__ out) {
-    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<kBf16>];
-    const Lane L = lane_map<kReceiverWaves>(nblocks);
-    float R[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j) R[j] = 0.0f;
-    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
-    sum_peers<kFma>(L, nblocks, peers, k, wl, R);
-    receiver_transform<kFwht, kBf16>(L, wl, R);
-    store_out<kBf16>(L, nblocks, wl, out, R);
 }
 
 
@@ -907,14 +894,16 @@ struct NarrowLane {
     bool valid;
 };
 
-template <int kWaves>
+// kEighthHigh: the eighth in lane bits 3-5 (p = lane bits 0-2), where the
+// receivers' transform exchanges it; otherwise in lane bits 0-2.
+template <int kWaves, bool kEighthHigh = false>
 __device__ __forceinline__ NarrowLane narrow_map(int64_t nblocks) {
     NarrowLane L;
     L.lane = threadIdx.x & (kWave - 1);
     const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     L.tile = ((int64_t)blockIdx.x * kWaves + wave_in_wg) * kNarrowBlocks;
-    L.p = L.lane >> 3;
-    L.e = L.lane & 7;
+    L.p = kEighthHigh ? (L.lane & 7) : (L.lane >> 3);
+    L.e = kEighthHigh ? (L.lane >> 3) : (L.lane & 7);
     L.b = L.tile + L.p;
     L.valid = L.b < nblocks;
     L.bl = L.valid ? L.b : nblocks - 1;  // lanes past the end compute on the last block, never store
@@ -996,6 +985,156 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_narrow_kern
         TileStore(micro, L.tile, nblocks, 16, kNarrowBlocks).b16(16 * L.p + 2 * L.e, (unsigned short)(mw & 0xFFFFu));
         if (L.e == 0) TileStore(block, L.tile, nblocks, 4, kNarrowBlocks).b32(4 * L.p, as_u(s));
     }
+}
+
+// ------------------------------------------- receiver reduce, narrow layout
+// Eight blocks per wavefront; lane l works on block p = l & 7 and its eighth
+// e = l >> 3 (element bits 5-7 in lane bits 3-5): 32 accumulator registers
+// (element bits 0-4).  Every peer's codes arrive in one contiguous 1 KiB load.
+// The inverse transform runs its first five stages in registers, then brings
+// element bits 5, 6 and 7 into register bit 4 one at a time -- lane bit 3 by a
+// row rotation (DPP), lane bits 4 and 5 by lane swaps -- each followed by its
+// stage; afterwards register r holds element (r & 15) + 16 f + 128 (r >> 4),
+// f = l >> 3, i.e. two runs of 16 consecutive values per lane.
+
+// Exchange lane bit 3 with register bit 4 (pairs r, r + 16): lanes with bit 3
+// clear receive the partner's r into r + 16, lanes with it set the partner's
+// r + 16 into r (DPP row rotation by 8 = the lane eight apart, written per bank).
+__device__ __forceinline__ void swap_lane3_reg4(float (&R)[32]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const unsigned a = as_u(R[r]), b = as_u(R[r + 16]);
+        const unsigned b2 = (unsigned)__builtin_amdgcn_update_dpp((int)b, (int)a, 0x128, 0xF, 0x3, false);
+        const unsigned a2 = (unsigned)__builtin_amdgcn_update_dpp((int)a, (int)b, 0x128, 0xF, 0xC, false);
+        R[r] = as_f(a2);
+        R[r + 16] = as_f(b2);
+    }
+}
+
+template <int H>
+__device__ __forceinline__ void stage32(float (&R)[32]) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+        if ((j & H) == 0) {
+            const float a = R[j], b = R[j + H];
+            R[j] = a + b;
+            R[j + H] = a - b;
+        }
+}
+
+template <bool kFwht>
+__device__ __forceinline__ void narrow_receiver_transform(float (&R)[32]) {
+    if constexpr (kFwht) {
+        stage32<1>(R);
+        stage32<2>(R);
+        stage32<4>(R);
+        stage32<8>(R);
+        stage32<16>(R);   // element bit 4
+    }
+    swap_lane3_reg4(R);
+    if constexpr (kFwht) stage32<16>(R);  // element bit 5
+#pragma unroll
+    for (int r = 0; r < 16; ++r) swap16(R[r], R[r + 16]);
+    if constexpr (kFwht) stage32<16>(R);  // element bit 6
+#pragma unroll
+    for (int r = 0; r < 16; ++r) swap32(R[r], R[r + 16]);
+    if constexpr (kFwht) {
+        stage32<16>(R);  // element bit 7
+#pragma unroll
+        for (int j = 0; j < 32; ++j) R[j] *= 0.0625f;
+    }
+}
+
+// R[j] = R[j] + E2M1(code j) * S_g with one fused multiply-add.
+__device__ __forceinline__ void dequant_fma_narrow(const NarrowPayload &P, float (&R)[32]) {
+    const unsigned C[4] = {P.c.x, P.c.y, P.c.z, P.c.w};
+    const float S[2] = {P.s * e4m3_value<0>(P.m), P.s * e4m3_value<1>(P.m)};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float Sg = S[w >> 1];
+        static_for<4>([&](auto sel) {
+            const auto f = e2m1_values<decltype(sel)::value>(C[w]);
+            const int j = 8 * w + 2 * decltype(sel)::value;
+            R[j] = fmaf(f[0], Sg, R[j]);
+            R[j + 1] = fmaf(f[1], Sg, R[j + 1]);
+        });
+    }
+}
+
+constexpr int kNarrowOutChunks = 264;  // fp32: 4 blocks of 65 chunks; bf16: 8 of 33
+
+// Output through the wavefront's LDS region so that every store writes 1 KiB.
+template <bool kBf16>
+__device__ __forceinline__ void narrow_store_out(const NarrowLane &L, int64_t nblocks, uint4 *__restrict__ lds,
+                                                 void *__restrict__ out, const float (&R)[32]) {
+    const int lane = L.lane, p = L.p, f = L.e;
+    if constexpr (kBf16) {
+        // a block is 32 chunks of 8 bf16 (stride 33); run h (registers 16 h ..) is
+        // chunks 16 h + 2 f, + 1
+        uint4 *dst = lds + 33 * p + 2 * f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int j = 16 * h + 8 * c;
+                dst[16 * h + c] = make_uint4(bf16_rne_pair(R[j], R[j + 1]), bf16_rne_pair(R[j + 2], R[j + 3]),
+                                             bf16_rne_pair(R[j + 4], R[j + 5]), bf16_rne_pair(R[j + 6], R[j + 7]));
+            }
+        wave_lds_sync();
+        const uint4 *src = lds + 33 * (lane >> 5) + (lane & 31);
+        const TileStore dst_g(out, L.tile, nblocks, 512, kNarrowBlocks);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {  // blocks 2u, 2u + 1
+            const int b = 2 * u + (lane >> 5);
+            const uint4 v = src[66 * u];
+            if (L.tile + b < nblocks) dst_g.b128(16 * (32 * b + (lane & 31)), v);
+        }
+    } else {
+        // a block is 64 chunks of 4 fp32 (stride 65); run h is chunks 32 h + 4 f .. + 3;
+        // two rounds of four blocks
+        const TileStore dst_g(out, L.tile, nblocks, 1024, kNarrowBlocks);
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            if ((p >> 2) == rd) {
+                uint4 *dst = lds + 65 * (p & 3) + 4 * f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int j = 16 * h + 4 * c;
+                        dst[32 * h + c] = make_uint4(as_u(R[j]), as_u(R[j + 1]), as_u(R[j + 2]), as_u(R[j + 3]));
+                    }
+            }
+            wave_lds_sync();
+            const uint4 *src = lds + lane;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int b = 4 * rd + u;
+                const uint4 v = src[65 * u];
+                if (L.tile + b < nblocks) dst_g.b128(16 * (64 * b + lane), v);
+            }
+            wave_lds_sync();
+        }
+    }
+}
+
+template <bool kFwht, bool kBf16>
+__global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_narrow_kernel(
+    Peers peers, int k, int64_t nblocks, void *__restrict__ out) {
+    __shared__ uint4 lds[kReceiverWaves * kNarrowOutChunks];
+    const NarrowLane L = narrow_map<kReceiverWaves, true>(nblocks);
+    uint4 *wl = lds + (threadIdx.x / kWave) * kNarrowOutChunks;
+    float R[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) R[j] = 0.0f;
+    NarrowPayload P = load_narrow(L, peers.codes[0], peers.micro[0], peers.block[0]);
+    for (int p = 0; p < k; ++p) {
+        const NarrowPayload cur = P;
+        if (p + 1 < k) P = load_narrow(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
+        dequant_fma_narrow(cur, R);
+    }
+    narrow_receiver_transform<kFwht>(R);
+    narrow_store_out<kBf16>(L, nblocks, wl, out, R);
 }
 
 // --------------------------------------------------- MXFP4-style variant
@@ -1249,11 +1388,11 @@ int fp4q_decompress_accumulate_ex(int k, const uint8_t *const *codes,
     }
     void *args[] = {&peers, &k, &nb, &out};
     const bool fw = !(flags & FP4Q_FLAG_NO_FWHT), bf = out_dtype == FP4Q_OUT_BF16;
-    const void *fn = fw ? (bf ? (const void *)&accumulate_kernel<true, true>
-                              : (const void *)&accumulate_kernel<true, false>)
-                        : (bf ? (const void *)&accumulate_kernel<false, true>
-                              : (const void *)&accumulate_kernel<false, false>);
-    return launch(fn, nb, kReceiverWaves, args, stream);
+    const void *fn = fw ? (bf ? (const void *)&accumulate_narrow_kernel<true, true>
+                              : (const void *)&accumulate_narrow_kernel<true, false>)
+                        : (bf ? (const void *)&accumulate_narrow_kernel<false, true>
+                              : (const void *)&accumulate_narrow_kernel<false, false>);
+    return launch(fn, nb, kReceiverWaves, args, stream, kNarrowBlocks);
 }
 
 int fp4q_decompress_accumulate(int k, const uint8_t *const *codes,

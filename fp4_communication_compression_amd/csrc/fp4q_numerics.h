@@ -13,6 +13,10 @@
 //                 two, 1 in the dual-scale kernels), saturating at 6, keeping
 //                 the sign of v;
 //   e2m1_values / e4m3_value   exact decodes;
+//   e2m1_halves   the same E2M1 values as binary16 (exact: every E2M1 value
+//                 times a power of two in [2^-14, 2^4] is a binary16 normal);
+//   fma_half      fma(h, b, c) of a binary16 h and binary32 b, c, rounded once
+//                 to binary32, exactly as fmaf((float)h, b, c);
 //   bf16_rne_pair round-to-nearest-even to bfloat16.
 #pragma once
 
@@ -67,6 +71,20 @@ __device__ __forceinline__ unsigned e2m1_pair(unsigned old, float v0, float v1, 
 template <int kSel>
 __device__ __forceinline__ auto e2m1_values(unsigned w, float scale = 1.0f) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, kSel);
+}
+
+// Values of the two E2M1 codes in byte kSel of w as binary16 (low nibble in
+// element 0), times scale (a power of two keeping them binary16 normals).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <int kSel>
+__device__ __forceinline__ f16x2 e2m1_halves(unsigned w, float scale = 1.0f) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, kSel);
+}
+
+// fma with a binary16 first factor (one mixed-precision instruction): the
+// conversion of h is exact, so the result is fmaf((float)h, b, c).
+__device__ __forceinline__ float fma_half(_Float16 h, float b, float c) {
+    return __builtin_fmaf((float)h, b, c);
 }
 
 // Two fp32 values rounded to nearest-even bfloat16, lo in the low half

@@ -203,6 +203,49 @@ __global__ __launch_bounds__(kThreads) void micro_div_random(uint64_t seed, uint
     report(res, bad, first);
 }
 
+// The binary16 decode and mixed-precision fused multiply-add against the
+// binary32 ones, on random operands: code c (4 bits), b and c with random bit
+// patterns (finite), decoded at scale 2^k for k in {0, -4}.  Checks, bit for bit
+// (NaN against NaN): fma_half(h, b, c) == fmaf(v, b, c) and
+// fma_half(h, b, -0) == v * b, where h and v are the binary16 and binary32
+// decodes of the same code.
+__device__ __forceinline__ bool same_bits(float a, float b) {
+    return as_u(a) == as_u(b) || (a != a && b != b);
+}
+
+__device__ __forceinline__ float random_finite(uint64_t r) {
+    uint32_t u = (uint32_t)r;
+    if ((u & 0x7F800000u) == 0x7F800000u) u ^= 0x40000000u;  // no Inf or NaN
+    // one draw in four from a narrower, typical exponent range [2^-40, 2^40)
+    if (((r >> 32) & 3u) == 0) u = (u & 0x807FFFFFu) | ((uint32_t)(87 + ((r >> 40) % 80u)) << 23);
+    return as_f(u);
+}
+
+__global__ __launch_bounds__(kThreads) void half_fma_random(uint64_t seed, uint64_t begin, uint64_t count,
+                                                             Result *res) {
+    const uint64_t base = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    unsigned long long bad = 0, first = ~0ull;
+#pragma unroll 4
+    for (int j = 0; j < kPer; ++j) {
+        const uint64_t i = base + j;
+        if (i >= count) break;
+        const uint64_t r0 = splitmix64(seed ^ (3 * (begin + i))), r1 = splitmix64(seed ^ (3 * (begin + i) + 1)),
+                       r2 = splitmix64(seed ^ (3 * (begin + i) + 2));
+        const unsigned code = (unsigned)(r2 >> 60) & 15u;
+        const float scale = (r2 >> 59) & 1u ? 0.0625f : 1.0f;
+        const float b = random_finite(r0), c = ((r2 >> 58) & 1u) ? random_finite(r1) : ((r2 >> 57) & 1u ? -0.0f : 0.0f);
+        const float v = e2m1_values<0>(code | (code << 4), scale)[0];
+        const _Float16 h = e2m1_halves<0>(code | (code << 4), scale)[0];
+        const bool ok = same_bits(fma_half(h, b, c), fmaf(v, b, c)) && same_bits(fma_half(h, b, -0.0f), v * b) &&
+                        same_bits((float)h, v);
+        if (!ok) {
+            ++bad;
+            first = first < begin + i ? first : begin + i;
+        }
+    }
+    report(res, bad, first);
+}
+
 // bf16_rne_pair against integer round-to-nearest-even on the bit pattern
 // (finite inputs; overflow rounds to infinity, as the integer form gives).
 __device__ __forceinline__ unsigned bf16_expect(uint32_t u) {
@@ -250,7 +293,9 @@ __global__ __launch_bounds__(kThreads) void eval_kernel(int what, const float *_
 }
 
 // Decode tables: out[0..255] = e4m3_value of every byte; then, for each of
-// nscales scales, the 16 E2M1 values at that scale.  One thread per entry.
+// nscales scales, the 16 E2M1 values at that scale; then the same through the
+// binary16 decode (meaningful where the values are binary16 normals).  One
+// thread per entry.
 __global__ __launch_bounds__(kThreads) void decode_kernel(const float *__restrict__ scales, int nscales,
                                                            float *__restrict__ out) {
     const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -261,6 +306,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const float *__restric
         // code c in both nibbles of byte 0: the low one decodes to f[0]
         const auto f = e2m1_values<0>((unsigned)(c | (c << 4)), scales[s]);
         out[i] = f[0];
+    } else if (i < 256 + 32 * nscales) {
+        const int s = (i - 256 - 16 * nscales) / 16, c = (i - 256) % 16;
+        out[i] = (float)e2m1_halves<0>((unsigned)(c | (c << 4)), scales[s])[0];
     }
 }
 
@@ -314,6 +362,12 @@ int ic_micro_div_random(uint64_t seed, uint64_t begin, uint64_t count, void *res
     return launch_sweep((const void *)&micro_div_random, args, count, stream);
 }
 
+int ic_half_fma_random(uint64_t seed, uint64_t begin, uint64_t count, void *res, void *stream) {
+    if (!res || count > (1ull << 32)) return -1;
+    void *args[] = {&seed, &begin, &count, &res};
+    return launch_sweep((const void *)&half_fma_random, args, count, stream);
+}
+
 int ic_bf16_sweep(uint64_t begin, uint64_t count, void *res, void *stream) {
     if (!res || count > (1ull << 32)) return -1;
     void *args[] = {&begin, &count, &res};
@@ -328,10 +382,10 @@ int ic_eval(int what, const float *in_dev, int64_t n, uint32_t *out_dev, void *s
     return e == hipSuccess ? 0 : -2;
 }
 
-// out_dev: 256 + 16 * nscales floats.
+// out_dev: 256 + 32 * nscales floats.
 int ic_decode_tables(const float *scales_dev, int nscales, float *out_dev, void *stream) {
     if (!scales_dev || !out_dev || nscales < 0 || nscales > 4096) return -1;
-    const int n = 256 + 16 * nscales;
+    const int n = 256 + 32 * nscales;
     void *args[] = {&scales_dev, &nscales, &out_dev};
     const hipError_t e = hipLaunchKernel((const void *)&decode_kernel, dim3((n + kThreads - 1) / kThreads),
                                          dim3(kThreads), args, 0, (hipStream_t)stream);

@@ -38,27 +38,30 @@ __global__ __launch_bounds__(kWave * kDecompressWaves<kBf16>) void twin_decompre
     store_out<kBf16>(L, nblocks, wl, out, R);
 }
 
-// accumulate_kernel<true, false>'s traffic: k payloads loaded and re-dealt
-// through LDS exactly as sum_peers does, then the fp32 output as decompress.
+// accumulate_narrow_kernel<true, false>'s traffic: k payloads loaded as the
+// narrow layout loads them (one contiguous 1 KiB of codes per peer, a 2-byte
+// micro-scale pair and the block scale per lane), then the fp32 output through
+// LDS in the same two rounds.
 __global__ __launch_bounds__(kWave * kReceiverWaves) void twin_accumulate_kernel(
     Peers peers, int k, int64_t nblocks, float *__restrict__ out) {
-    __shared__ uint4 lds[kReceiverWaves * kReceiverChunks<false>];
-    const Lane L = lane_map<kReceiverWaves>(nblocks);
-    uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<false>;
-    unsigned w[8] = {0, 0, 0, 0, 0, 0, 0, 0}, salt = 0;
-    PayloadRegs buf = load_payload<true>(L, nblocks, peers.codes[0], peers.micro[0], peers.block[0]);
+    __shared__ uint4 lds[kReceiverWaves * kNarrowOutChunks];
+    const NarrowLane L = narrow_map<kReceiverWaves, true>(nblocks);
+    uint4 *wl = lds + (threadIdx.x / kWave) * kNarrowOutChunks;
+    unsigned w[4] = {0, 0, 0, 0}, salt = 0;
+    NarrowPayload P = load_narrow(L, peers.codes[0], peers.micro[0], peers.block[0]);
     for (int p = 0; p < k; ++p) {
-        redeal_codes(L, wl, buf);
-        const unsigned c[8] = {buf.c0.x, buf.c0.y, buf.c0.z, buf.c0.w, buf.c1.x, buf.c1.y, buf.c1.z, buf.c1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] ^= c[i];
-        salt ^= buf.lo ^ buf.hi ^ as_u(buf.s);
-        if (p + 1 < k) buf = load_payload<true>(L, nblocks, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
+        const NarrowPayload cur = P;
+        if (p + 1 < k) P = load_narrow(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
+        w[0] ^= cur.c.x;
+        w[1] ^= cur.c.y;
+        w[2] ^= cur.c.z;
+        w[3] ^= cur.c.w;
+        salt ^= cur.m ^ as_u(cur.s);
     }
-    float R[64];
-    fill_registers(w, salt, R);
-    wave_lds_sync();  // the re-deal's reads of the region are done
-    store_out<false>(L, nblocks, wl, out, R);
+    float R[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) R[j] = as_f(w[j & 3] ^ (salt + (unsigned)j));
+    narrow_store_out<false>(L, nblocks, wl, out, R);
 }
 
 // compress_kernel<true>'s traffic: the bf16 tile through LDS as load_widen
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void twin_compress_kernel(
 }
 
 // Plain streams over nbytes (a multiple of 16 KiB): every wavefront moves
-// 16 KiB as sixteen 1 KiB instructions, loads on the non-temporal path (kept
-// alive by one 16-byte store per wavefront) or stores with the library's
+// 16 KiB as sixteen 1 KiB instructions, loads on the non-temporal path (all
+// folded into one 16-byte store per wavefront) or stores with the library's
 // policy.
 __global__ __launch_bounds__(256) void twin_read_kernel(const uint4 *__restrict__ in, int64_t nwaves,
                                                         uint4 *__restrict__ sink) {
@@ -110,6 +113,15 @@ __global__ __launch_bounds__(256) void twin_read_kernel(const uint4 *__restrict_
         acc.y ^= v.y;
         acc.z ^= v.z;
         acc.w ^= v.w;
+    }
+    // every lane's loads feed the stored word (a store by one lane alone would
+    // let the compiler move the other lanes' loads under its branch)
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        acc.x ^= (unsigned)__shfl_xor((int)acc.x, m);
+        acc.y ^= (unsigned)__shfl_xor((int)acc.y, m);
+        acc.z ^= (unsigned)__shfl_xor((int)acc.z, m);
+        acc.w ^= (unsigned)__shfl_xor((int)acc.w, m);
     }
     if (lane == 0) sink[wv] = acc;
 }
@@ -155,7 +167,9 @@ int twin_accumulate(int k, const uint8_t *const *codes, const uint8_t *const *mi
         peers.block[p] = block[p];
     }
     void *args[] = {&peers, &k, &nb, &out};
-    return launch((const void *)&twin_accumulate_kernel, nb, kReceiverWaves, args, stream) == FP4Q_OK ? 0 : -2;
+    return launch((const void *)&twin_accumulate_kernel, nb, kReceiverWaves, args, stream, kNarrowBlocks) == FP4Q_OK
+               ? 0
+               : -2;
 }
 
 int twin_compress(const uint16_t *in, int64_t rows, int64_t row_len, uint8_t *codes, uint8_t *micro,

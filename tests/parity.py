@@ -58,3 +58,13 @@ def check_rowwise(gpu: np.ndarray, ref: np.ndarray, rel: float = 1e-6, magnitude
     with np.errstate(invalid="ignore", divide="ignore"):
         ratio = np.where(scale > 0, err / scale, 0.0)
     return float(ratio.max()) if ratio.size else 0.0
+
+
+def check_compress_exact(gpu, ref) -> dict:
+    """check_compress, and no tolerated mismatch either: every code and every
+    micro-scale equal to the oracle's (the kernels follow the oracle's fp32
+    operation order, so no value sits on the other side of a boundary)."""
+    st = check_compress(gpu, ref)
+    assert st["code_mismatch"] == 0 and st["micro_mismatch"] == 0, \
+        "near-boundary mismatches where every byte should be exact: %s" % st
+    return st

@@ -142,3 +142,6 @@ def test_kernel_families():
     assert bench._short(ns + "requantize_narrow_kernel(x)") == "requantize"
     assert bench._short(ns + "requantize_kernel<true>(x)") == "requantize_local"
     assert bench._short(ns + "compress_mx_kernel<true>(x)") == "compress_mx"
+    assert bench._short(ns + "accumulate_narrow_kernel<true, false>(x)") == "accumulate"
+    assert bench.KERNEL_NAME.search(ns + "accumulate_narrow_kernel<true, false>(x)").group(1) \
+        == "accumulate_narrow_kernel<true, false>"

@@ -105,6 +105,7 @@ def ic():
     L.ic_scale_sweep.argtypes = [U64, U64, P, P]
     L.ic_micro_div_random.argtypes = [U64, U64, U64, P, P]
     L.ic_bf16_sweep.argtypes = [U64, U64, P, P]
+    L.ic_half_fma_random.argtypes = [U64, U64, U64, P, P]
     L.ic_eval.argtypes = [I, P, ctypes.c_int64, P, P]
     L.ic_decode_tables.argtypes = [P, I, P, P]
     return L, torch
@@ -210,6 +211,18 @@ def test_micro_scale_division_random_blocks(ic):
 
 
 @pytest.mark.gpu
+def test_binary16_decode_and_mixed_fma_random(ic):
+    """The receivers may decode E2M1 to binary16 and use a mixed-precision fused
+    multiply-add: on 2^32 random (code, b, c) draws (scale 1 or 1/16, b and c any
+    finite fp32 or typical magnitudes, c also +-0) it equals the binary32 decode
+    and fmaf bit for bit, and fma(h, b, -0) equals the rounded product."""
+    L, _ = ic
+    bad, first = _sweep(ic, "binary16 decode + mixed fma, random", [(0, 1 << 32)],
+                        lambda b, c, r, s: L.ic_half_fma_random(0xF16, b, c, r, s))
+    assert bad == 0, "binary16 decode / mixed fma differs at random index %d" % first
+
+
+@pytest.mark.gpu
 def test_bf16_rounding_every_finite_float(ic):
     L, _ = ic
     bad, first = _sweep(ic, "bf16 rounding", FINITE, lambda b, c, r, s: L.ic_bf16_sweep(b, c, r, s))
@@ -262,7 +275,7 @@ def test_decode_tables(ic):
     L, torch = ic
     ks = np.arange(-126, 128)
     scales = torch.tensor(np.ldexp(1.0, ks).astype(np.float32), device="cuda")
-    out = torch.empty(256 + 16 * ks.size, dtype=torch.float32, device="cuda")
+    out = torch.empty(256 + 32 * ks.size, dtype=torch.float32, device="cuda")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     assert L.ic_decode_tables(ctypes.c_void_p(scales.data_ptr()), ks.size,
                               ctypes.c_void_p(out.data_ptr()), stream) == 0
@@ -275,4 +288,8 @@ def test_decode_tables(ic):
     e2 = np.array([oracle.e2m1_decode(c) for c in range(16)], np.float64)
     with np.errstate(over="ignore"):   # 3 x 2^127 and 6 x 2^127 round to infinity
         want = (e2[None, :] * np.ldexp(1.0, ks)[:, None]).astype(np.float32).reshape(-1)
-    np.testing.assert_array_equal(o[256:].view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(o[256:256 + 16 * ks.size].view(np.uint32), want.view(np.uint32))
+    # binary16 decode, at the scales where every value is a binary16 normal (2^-14 .. 2^4 x 0.5..6)
+    half = o[256 + 16 * ks.size:].reshape(ks.size, 16)
+    normal = (ks >= -13) & (ks <= 3)
+    np.testing.assert_array_equal(half[normal].view(np.uint32), want.reshape(ks.size, 16)[normal].view(np.uint32))
