@@ -210,10 +210,13 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> str:
            "|---|---|---|---|---|---|---|"]
     traffic = {}
     for k in ("compress", "decompress", "accumulate", "requantize", "requantize_local"):
-        # only launches of the workload each figure is defined for (one thread per 64 elements)
+        # only launches of the workload each figure is defined for: one thread per
+        # 64 elements in the wide layout, per 32 in the narrow one (accumulate and
+        # the re-quantise without a local slice), up to a last partial workgroup
         head = k in ("compress", "decompress")
-        want_grid = (32768 * 4096 if head else REDUCE_N) // 64
-        if k not in fetch or k not in write or grids[k] != want_grid:
+        per_lane = 32 if k in ("accumulate", "requantize") else 64
+        want_grid = (32768 * 4096 if head else REDUCE_N) // per_lane
+        if k not in fetch or k not in write or not want_grid <= grids[k] < want_grid + 1024:
             continue
         t = fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale
         traffic[k] = int(round(t))

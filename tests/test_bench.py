@@ -81,6 +81,29 @@ def test_counter_summary_scales_by_the_copy_reference(tmp_path):
     assert "| compress | 32768x4096 |" in text and "| 1.000 |" in text
 
 
+ACC = "void (anonymous namespace)::accumulate_narrow_kernel<true, false>(Peers, int, long, float*)"
+REQ = "void (anonymous namespace)::requantize_narrow_kernel(Peers, int, long, uint4*, unsigned int*, float*)"
+REQ_LOCAL = "void (anonymous namespace)::requantize_kernel<true>(Peers, int, long, uint4*, unsigned int*, float*)"
+
+
+def test_counter_summary_receivers_at_their_layouts_grids(tmp_path):
+    # accumulate and the re-quantise without a local slice run one thread per 32
+    # elements, the re-quantise with one a thread per 64; launches of other
+    # grids are another workload and give no figure
+    n, rb = bench.REDUCE_N, bench._receiver_bytes()
+    fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE", [
+        (COPY, 131072, KIB / 2), (COPY, 131072, KIB / 2), (COPY, 131072, KIB / 2),
+        (ACC, n // 32, (rb["accumulate"] - 4 * n) / 2048),
+        (REQ, n // 32, 100.0), (REQ_LOCAL, n // 32, 100.0)])
+    write = _counter_dir(tmp_path, "w", "WRITE_SIZE", [
+        (COPY, 131072, KIB), (COPY, 131072, KIB), (COPY, 131072, KIB),
+        (ACC, n // 32, 4 * n / 1024), (REQ, n // 32, 10.0), (REQ_LOCAL, n // 32, 10.0)])
+    traffic = dict(kv.split("=") for kv in bench.summarize_counters(fetch, write).splitlines()[-1].split()[1:])
+    assert int(traffic["accumulate"]) == rb["accumulate"]
+    assert int(traffic["requantize"]) == 2 * 100 * 1024 + 10 * 1024
+    assert "requantize_local" not in traffic     # a narrow grid is not its workload
+
+
 def test_counter_summary_reference_is_the_largest_copies(tmp_path):
     # smaller copies (tensor clones) share the grid-strided copy kernel's grid and
     # are left out; the reference needs its three copies
