@@ -890,7 +890,9 @@ constexpr int kNarrowBlocks = 8;
 
 struct NarrowLane {
     int lane, p, e;
-    int64_t tile, b, bl;
+    int64_t tile, b;
+    int nvalid;           // blocks of the tile that exist (wave-uniform, 0 .. 8)
+    unsigned oc, om, ob;  // byte offsets in the tile of the lane's codes, micro-scale pair, block scale
     bool valid;
 };
 
@@ -906,7 +908,12 @@ __device__ __forceinline__ NarrowLane narrow_map(int64_t nblocks) {
     L.e = kEighthHigh ? (L.lane >> 3) : (L.lane & 7);
     L.b = L.tile + L.p;
     L.valid = L.b < nblocks;
-    L.bl = L.valid ? L.b : nblocks - 1;  // lanes past the end compute on the last block, never store
+    const int64_t left = nblocks - L.tile;
+    L.nvalid = left <= 0 ? 0 : left < kNarrowBlocks ? (int)left : kNarrowBlocks;
+    const unsigned chunk = (unsigned)L.p * 8u + (unsigned)L.e;
+    L.oc = 16u * chunk;
+    L.om = 2u * chunk;
+    L.ob = 4u * (unsigned)L.p;
     return L;
 }
 
@@ -924,18 +931,67 @@ struct NarrowPayload {
     float s;
 };
 
+// One peer's payload for the lane, through buffer descriptors over the
+// wavefront's tile (built in scalar registers from the peer's base pointers, so
+// a load costs no vector address arithmetic); lanes of blocks past the end read
+// zeros (outside the descriptors' range) and never store.
+constexpr int kLoadNt = 2;  // the non-temporal cache policy
 __device__ __forceinline__ NarrowPayload load_narrow(const NarrowLane &L, const uint4 *__restrict__ codes,
                                                      const uint4 *__restrict__ micro,
                                                      const float *__restrict__ block) {
+    const auto rsrc = [&](const void *base, int bytes_per_block) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char *>(reinterpret_cast<const char *>(base)) + L.tile * bytes_per_block, 0,
+            L.nvalid * bytes_per_block, 0x00020000);
+    };
     NarrowPayload P;
-    P.c = load_nt(codes + L.bl * 8 + L.e);
-    P.m = reinterpret_cast<const unsigned short *>(micro)[L.bl * 8 + L.e];
-    P.s = block[L.bl];
+    const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rsrc(codes, 128), (int)L.oc, 0, kLoadNt);
+    P.c = make_uint4(c[0], c[1], c[2], c[3]);
+    P.m = __builtin_amdgcn_raw_buffer_load_b16(rsrc(micro, 16), (int)L.om, 0, 0);
+    P.s = as_f(__builtin_amdgcn_raw_buffer_load_b32(rsrc(block, 4), (int)L.ob, 0, 0));
     return P;
 }
 
+// add(payload of peer p, first) for p = 0 .. k - 1 in order (first: an
+// integral constant, true for peer 0 only, whose add initialises the
+// accumulator), with the next peer's loads in flight while a peer is added
+// (k >= 1, wave-uniform).  Two payload slots taken in turn, each reloaded
+// unconditionally inside the loop, let every load write straight into the
+// registers it is added from (a rolled loop with one slot, or a conditional
+// reload, would copy the slot every peer).  The scheduling barriers keep each
+// load issued before the previous peer's arithmetic (left alone, the compiler
+// sinks it below that).
+using First = std::integral_constant<bool, true>;
+using Later = std::integral_constant<bool, false>;
+template <typename Add>
+__device__ __forceinline__ void for_each_peer_narrow(const NarrowLane &L, const Peers &peers, int k, Add &&add) {
+    const auto load = [&](int p) { return load_narrow(L, peers.codes[p], peers.micro[p], peers.block[p]); };
+    NarrowPayload A = load(0), B = A;
+    if (k > 1) B = load(1);
+    __builtin_amdgcn_sched_barrier(0);
+    add(A, First{});
+    int p = 1;  // B holds peer p
+    for (; p + 2 < k; p += 2) {
+        A = load(p + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        add(B, Later{});
+        B = load(p + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        add(A, Later{});
+    }
+    if (p < k) {  // peer p (in B), and peer p + 1 if there is one
+        const bool two = p + 1 < k;
+        A = B;
+        if (two) A = load(p + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        add(B, Later{});
+        if (two) add(A, Later{});
+    }
+}
+
 // R[j] = R[j] + E2M1(code j) * S_g: a rounded product, then a rounded sum (the
-// order the re-quantisation defines).
+// order the re-quantisation defines); kFirst: R[j] = +0 + E2M1(code j) * S_g.
+template <bool kFirst>
 __device__ __forceinline__ void dequant_add_narrow(const NarrowPayload &P, float (&R)[32]) {
     const unsigned C[4] = {P.c.x, P.c.y, P.c.z, P.c.w};
     const float S[2] = {P.s * e4m3_value<0>(P.m), P.s * e4m3_value<1>(P.m)};
@@ -946,9 +1002,10 @@ __device__ __forceinline__ void dequant_add_narrow(const NarrowPayload &P, float
             const auto f = e2m1_values<decltype(sel)::value>(C[w]);
             const int j = 8 * w + 2 * decltype(sel)::value;
             const float p0 = f[0] * Sg, p1 = f[1] * Sg;  // built without contraction
-            R[j] = R[j] + p0;
-            R[j + 1] = R[j + 1] + p1;
+            R[j] = (kFirst ? 0.0f : R[j]) + p0;
+            R[j + 1] = (kFirst ? 0.0f : R[j + 1]) + p1;
         });
+        __builtin_amdgcn_sched_barrier(0);  // decode no further ahead than a dword
     }
 }
 
@@ -957,15 +1014,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_narrow_kern
     float *__restrict__ block) {
     const NarrowLane L = narrow_map<kReceiverWaves>(nblocks);
     float R[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) R[j] = 0.0f;
-    // one peer's loads in flight while the previous one is added (k is wave-uniform)
-    NarrowPayload P = load_narrow(L, peers.codes[0], peers.micro[0], peers.block[0]);
-    for (int p = 0; p < k; ++p) {
-        const NarrowPayload cur = P;
-        if (p + 1 < k) P = load_narrow(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
-        dequant_add_narrow(cur, R);
-    }
+    for_each_peer_narrow(L, peers, k, [&](const NarrowPayload &P, auto first) {
+        dequant_add_narrow<decltype(first)::value>(P, R);
+    });
 
     float a[2];
 #pragma unroll
@@ -1045,7 +1096,9 @@ __device__ __forceinline__ void narrow_receiver_transform(float (&R)[32]) {
     }
 }
 
-// R[j] = R[j] + E2M1(code j) * S_g with one fused multiply-add.
+// R[j] = R[j] + E2M1(code j) * S_g with one fused multiply-add (kFirst: added
+// to +0).
+template <bool kFirst>
 __device__ __forceinline__ void dequant_fma_narrow(const NarrowPayload &P, float (&R)[32]) {
     const unsigned C[4] = {P.c.x, P.c.y, P.c.z, P.c.w};
     const float S[2] = {P.s * e4m3_value<0>(P.m), P.s * e4m3_value<1>(P.m)};
@@ -1055,9 +1108,10 @@ __device__ __forceinline__ void dequant_fma_narrow(const NarrowPayload &P, float
         static_for<4>([&](auto sel) {
             const auto f = e2m1_values<decltype(sel)::value>(C[w]);
             const int j = 8 * w + 2 * decltype(sel)::value;
-            R[j] = fmaf(f[0], Sg, R[j]);
-            R[j + 1] = fmaf(f[1], Sg, R[j + 1]);
+            R[j] = fmaf(f[0], Sg, kFirst ? 0.0f : R[j]);
+            R[j + 1] = fmaf(f[1], Sg, kFirst ? 0.0f : R[j + 1]);
         });
+        __builtin_amdgcn_sched_barrier(0);  // decode no further ahead than a dword
     }
 }
 
@@ -1125,14 +1179,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_narrow_kern
     const NarrowLane L = narrow_map<kReceiverWaves, true>(nblocks);
     uint4 *wl = lds + (threadIdx.x / kWave) * kNarrowOutChunks;
     float R[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) R[j] = 0.0f;
-    NarrowPayload P = load_narrow(L, peers.codes[0], peers.micro[0], peers.block[0]);
-    for (int p = 0; p < k; ++p) {
-        const NarrowPayload cur = P;
-        if (p + 1 < k) P = load_narrow(L, peers.codes[p + 1], peers.micro[p + 1], peers.block[p + 1]);
-        dequant_fma_narrow(cur, R);
-    }
+    for_each_peer_narrow(L, peers, k, [&](const NarrowPayload &P, auto first) {
+        dequant_fma_narrow<decltype(first)::value>(P, R);
+    });
     narrow_receiver_transform<kFwht>(R);
     narrow_store_out<kBf16>(L, nblocks, wl, out, R);
 }
