@@ -180,6 +180,17 @@ struct TileStore {
     }
 };
 
+// A buffer descriptor over the wavefront's tile of an array with
+// bytes_per_block bytes per block: the bytes of the tile's nvalid existing
+// blocks (built in scalar registers; loads outside it read zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int64_t tile, int nvalid,
+                                                            int bytes_per_block) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(reinterpret_cast<const char *>(base)) + tile * bytes_per_block, 0,
+        nvalid * bytes_per_block, 0x00020000);
+}
+constexpr int kLoadNt = 2;  // the non-temporal cache policy
+
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
 __device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
 
@@ -574,31 +585,42 @@ struct PayloadRegs {
 };
 
 // The block's 16 micro-scale bytes arrive in one 16-byte load (the four lanes of
-// a block read the same 16 bytes); each lane keeps its two byte pairs.  kContig:
-// the codes in the contiguous order, for redeal_codes.
-template <bool kContig>
-__device__ __forceinline__ PayloadRegs load_payload(const Lane &L, int64_t nblocks,
-                                                    const uint4 *__restrict__ codes,
+// a block read the same 16 bytes); each lane keeps its two byte pairs.
+__device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *__restrict__ codes,
                                                     const uint4 *__restrict__ micro,
                                                     const float *__restrict__ block) {
     PayloadRegs P;
-    if constexpr (kContig) {
-        // tile chunk 64 j + lane = chunk lane & 7 of block 8 j + (lane >> 3), clamped
-        // to the last block in a ragged tile; redeal_codes gives the lane layout
-        const int64_t last = nblocks - 1;
-        const int64_t b0 = L.tile + (L.lane >> 3), b1 = b0 + 8;
-        P.c0 = load_nt(codes + (b0 < last ? b0 : last) * 8 + (L.lane & 7));
-        P.c1 = load_nt(codes + (b1 < last ? b1 : last) * 8 + (L.lane & 7));
-    } else {
-        const uint4 *src = codes + L.bl * 8 + L.q;
-        P.c0 = load_nt(src);
-        P.c1 = load_nt(src + 4);
-    }
+    const uint4 *src = codes + L.bl * 8 + L.q;
+    P.c0 = load_nt(src);
+    P.c1 = load_nt(src + 4);
     const uint4 m = micro[L.bl];
     const unsigned sh = 16u * (L.q & 1);
     P.lo = ((L.q >> 1) ? m.y : m.x) >> sh;
     P.hi = ((L.q >> 1) ? m.w : m.z) >> sh;
     P.s = block[L.bl];
+    return P;
+}
+
+// A peer's payload for the multi-peer kernels, through buffer descriptors over
+// the wavefront's tile: codes in the contiguous order (tile chunk 64 j + lane,
+// chunk lane & 7 of block 8 j + (lane >> 3); redeal_codes gives the lane
+// layout), the lane's two micro-scale pairs as 2-byte loads, the block scale.
+// Lanes of blocks past the end read zeros and never store.
+__device__ __forceinline__ PayloadRegs load_payload_tile(const Lane &L, int64_t nblocks,
+                                                         const uint4 *__restrict__ codes,
+                                                         const uint4 *__restrict__ micro,
+                                                         const float *__restrict__ block) {
+    const int64_t left = nblocks - L.tile;
+    const int nvalid = left <= 0 ? 0 : left < kTileBlocks ? (int)left : kTileBlocks;
+    const __amdgpu_buffer_rsrc_t rc = tile_rsrc(codes, L.tile, nvalid, 128), rm = tile_rsrc(micro, L.tile, nvalid, 16);
+    PayloadRegs P;
+    const u32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * L.lane, 0, kLoadNt);
+    const u32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(rc, 1024 + 16 * L.lane, 0, kLoadNt);
+    P.c0 = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+    P.c1 = make_uint4(c1[0], c1[1], c1[2], c1[3]);
+    P.lo = __builtin_amdgcn_raw_buffer_load_b16(rm, 16 * L.p + 2 * L.q, 0, 0);
+    P.hi = __builtin_amdgcn_raw_buffer_load_b16(rm, 16 * L.p + 8 + 2 * L.q, 0, 0);
+    P.s = as_f(__builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(block, L.tile, nvalid, 4), 4 * L.p, 0, 0));
     return P;
 }
 
@@ -767,7 +789,7 @@ __global__ __launch_bounds__(kWave * kDecompressWaves<kBf16>) void decompress_ke
     const Lane L = lane_map<kDecompressWaves<kBf16>>(nblocks);
     float R[64];
     uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
-    const PayloadRegs P = load_payload<false>(L, nblocks, codes, micro, block);
+    const PayloadRegs P = load_payload(L, codes, micro, block);
     const bool fold = kFwht && fold_sixteenth(P.s);
     dequant<kSet>(P, R, fold ? 0.0625f : 1.0f);
     receiver_transform<kFwht, kBf16>(L, wl, R, fold);
@@ -781,37 +803,55 @@ struct Peers {
     const float *block[FP4Q_MAX_PEERS];
 };
 
-// Sum of k payloads into R (as rounded products and rounded sums, kAdd) with
-// kInFlight payloads' loads outstanding: the loads of peer p + kInFlight are
-// issued as soon as peer p has been dequantised.  Codes are loaded contiguously
-// and re-dealt through the wavefront's LDS region lds (free during the sum, at
-// least 144 chunks).  k is wave-uniform, so every branch here is uniform.  One
-// payload in flight measured best: every further buffer costs 12 registers, and
-// the resident wavefronts those registers would allow hide more latency.
-#ifndef FP4Q_PEERS_IN_FLIGHT
-#define FP4Q_PEERS_IN_FLIGHT 1
-#endif
-constexpr int kInFlight = FP4Q_PEERS_IN_FLIGHT;
+// add(load(p), first) for p = 0 .. k - 1 in order (first: an integral constant,
+// true for peer 0 only), with the next peer's loads in flight while a peer is
+// added (k >= 1, wave-uniform).  Two payload slots taken in turn, each reloaded
+// unconditionally inside the loop, let every load write straight into the
+// registers it is added from (a rolled loop with one slot, or a conditional
+// reload, would copy the slot every peer).  The scheduling barriers keep each
+// load issued before the previous peer's arithmetic (left alone, the compiler
+// sinks it below that).
+using First = std::integral_constant<bool, true>;
+using Later = std::integral_constant<bool, false>;
+template <typename Load, typename Add>
+__device__ __forceinline__ void for_each_peer(int k, Load &&load, Add &&add) {
+    auto A = load(0), B = A;
+    if (k > 1) B = load(1);
+    __builtin_amdgcn_sched_barrier(0);
+    add(A, First{});
+    int p = 1;  // B holds peer p
+    for (; p + 2 < k; p += 2) {
+        A = load(p + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        add(B, Later{});
+        B = load(p + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        add(A, Later{});
+    }
+    if (p < k) {  // peer p (in B), and peer p + 1 if there is one
+        const bool two = p + 1 < k;
+        A = B;
+        if (two) A = load(p + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        add(B, Later{});
+        if (two) add(A, Later{});
+    }
+}
 
-template <DequantMode kMode>
+
+// R += the k payloads (rounded products added in peer order), k >= 0.  Codes
+// are loaded contiguously and re-dealt through the wavefront's LDS region lds
+// (free during the sum, at least 144 chunks).  k is wave-uniform, so every
+// branch here is uniform.
 __device__ __forceinline__ void sum_peers(const Lane &L, int64_t nblocks, const Peers &peers, int k,
                                           uint4 *__restrict__ lds, float (&R)[64]) {
-    PayloadRegs buf[kInFlight];
-#pragma unroll
-    for (int i = 0; i < kInFlight; ++i)
-        if (i < k) buf[i] = load_payload<true>(L, nblocks, peers.codes[i], peers.micro[i], peers.block[i]);
-    for (int p = 0; p < k; p += kInFlight) {
-#pragma unroll
-        for (int i = 0; i < kInFlight; ++i) {
-            if (p + i < k) {
-                redeal_codes(L, lds, buf[i]);
-                dequant<kMode>(buf[i], R);
-                const int nx = p + i + kInFlight;
-                if (nx < k)
-                    buf[i] = load_payload<true>(L, nblocks, peers.codes[nx], peers.micro[nx], peers.block[nx]);
-            }
-        }
-    }
+    if (k == 0) return;
+    for_each_peer(
+        k, [&](int p) { return load_payload_tile(L, nblocks, peers.codes[p], peers.micro[p], peers.block[p]); },
+        [&](PayloadRegs &P, auto) {
+            redeal_codes(L, lds, P);
+            dequant<kAdd>(P, R);
+        });
 }
 
 
@@ -863,7 +903,7 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     load_widen<false>(L, local, nblocks, lds, R);
     local_transform<kFwht>(R);
     wave_lds_sync();  // every lane has read its input chunks
-    sum_peers<kAdd>(L, nblocks, peers, k, lds, R);
+    sum_peers(L, nblocks, peers, k, lds, R);
 
     float s, t[4];
     unsigned mw, C[8];
@@ -935,58 +975,16 @@ struct NarrowPayload {
 // wavefront's tile (built in scalar registers from the peer's base pointers, so
 // a load costs no vector address arithmetic); lanes of blocks past the end read
 // zeros (outside the descriptors' range) and never store.
-constexpr int kLoadNt = 2;  // the non-temporal cache policy
 __device__ __forceinline__ NarrowPayload load_narrow(const NarrowLane &L, const uint4 *__restrict__ codes,
                                                      const uint4 *__restrict__ micro,
                                                      const float *__restrict__ block) {
-    const auto rsrc = [&](const void *base, int bytes_per_block) {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char *>(reinterpret_cast<const char *>(base)) + L.tile * bytes_per_block, 0,
-            L.nvalid * bytes_per_block, 0x00020000);
-    };
     NarrowPayload P;
-    const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rsrc(codes, 128), (int)L.oc, 0, kLoadNt);
+    const u32x4 c =
+        __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(codes, L.tile, L.nvalid, 128), (int)L.oc, 0, kLoadNt);
     P.c = make_uint4(c[0], c[1], c[2], c[3]);
-    P.m = __builtin_amdgcn_raw_buffer_load_b16(rsrc(micro, 16), (int)L.om, 0, 0);
-    P.s = as_f(__builtin_amdgcn_raw_buffer_load_b32(rsrc(block, 4), (int)L.ob, 0, 0));
+    P.m = __builtin_amdgcn_raw_buffer_load_b16(tile_rsrc(micro, L.tile, L.nvalid, 16), (int)L.om, 0, 0);
+    P.s = as_f(__builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(block, L.tile, L.nvalid, 4), (int)L.ob, 0, 0));
     return P;
-}
-
-// add(payload of peer p, first) for p = 0 .. k - 1 in order (first: an
-// integral constant, true for peer 0 only, whose add initialises the
-// accumulator), with the next peer's loads in flight while a peer is added
-// (k >= 1, wave-uniform).  Two payload slots taken in turn, each reloaded
-// unconditionally inside the loop, let every load write straight into the
-// registers it is added from (a rolled loop with one slot, or a conditional
-// reload, would copy the slot every peer).  The scheduling barriers keep each
-// load issued before the previous peer's arithmetic (left alone, the compiler
-// sinks it below that).
-using First = std::integral_constant<bool, true>;
-using Later = std::integral_constant<bool, false>;
-template <typename Add>
-__device__ __forceinline__ void for_each_peer_narrow(const NarrowLane &L, const Peers &peers, int k, Add &&add) {
-    const auto load = [&](int p) { return load_narrow(L, peers.codes[p], peers.micro[p], peers.block[p]); };
-    NarrowPayload A = load(0), B = A;
-    if (k > 1) B = load(1);
-    __builtin_amdgcn_sched_barrier(0);
-    add(A, First{});
-    int p = 1;  // B holds peer p
-    for (; p + 2 < k; p += 2) {
-        A = load(p + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        add(B, Later{});
-        B = load(p + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        add(A, Later{});
-    }
-    if (p < k) {  // peer p (in B), and peer p + 1 if there is one
-        const bool two = p + 1 < k;
-        A = B;
-        if (two) A = load(p + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        add(B, Later{});
-        if (two) add(A, Later{});
-    }
 }
 
 // R[j] = R[j] + E2M1(code j) * S_g: a rounded product, then a rounded sum (the
@@ -1014,9 +1012,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_narrow_kern
     float *__restrict__ block) {
     const NarrowLane L = narrow_map<kReceiverWaves>(nblocks);
     float R[32];
-    for_each_peer_narrow(L, peers, k, [&](const NarrowPayload &P, auto first) {
-        dequant_add_narrow<decltype(first)::value>(P, R);
-    });
+    for_each_peer(
+        k, [&](int p) { return load_narrow(L, peers.codes[p], peers.micro[p], peers.block[p]); },
+        [&](const NarrowPayload &P, auto first) { dequant_add_narrow<decltype(first)::value>(P, R); });
 
     float a[2];
 #pragma unroll
@@ -1179,9 +1177,9 @@ __global__ __launch_bounds__(kWave * kReceiverWaves) void accumulate_narrow_kern
     const NarrowLane L = narrow_map<kReceiverWaves, true>(nblocks);
     uint4 *wl = lds + (threadIdx.x / kWave) * kNarrowOutChunks;
     float R[32];
-    for_each_peer_narrow(L, peers, k, [&](const NarrowPayload &P, auto first) {
-        dequant_fma_narrow<decltype(first)::value>(P, R);
-    });
+    for_each_peer(
+        k, [&](int p) { return load_narrow(L, peers.codes[p], peers.micro[p], peers.block[p]); },
+        [&](const NarrowPayload &P, auto first) { dequant_fma_narrow<decltype(first)::value>(P, R); });
     narrow_receiver_transform<kFwht>(R);
     narrow_store_out<kBf16>(L, nblocks, wl, out, R);
 }

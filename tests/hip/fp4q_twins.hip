@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kWave * kDecompressWaves<kBf16>) void twin_decompre
     __shared__ uint4 lds[kDecompressWaves<kBf16> * kReceiverChunks<kBf16>];
     const Lane L = lane_map<kDecompressWaves<kBf16>>(nblocks);
     uint4 *wl = lds + (threadIdx.x / kWave) * kReceiverChunks<kBf16>;
-    const PayloadRegs P = load_payload<false>(L, nblocks, codes, micro, block);
+    const PayloadRegs P = load_payload(L, codes, micro, block);
     const unsigned w[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
     float R[64];
     fill_registers(w, P.lo ^ P.hi ^ as_u(P.s), R);
