@@ -267,15 +267,6 @@ __device__ __forceinline__ float block_lane_max(float v) {
     return fmaxf(a, b);
 }
 
-// 4x4 transpose over (lane bits 4-5) x (register index bits 0-1) of four values.
-template <typename T>
-__device__ __forceinline__ void transpose4(T &x0, T &x1, T &x2, T &x3) {
-    swap16(x0, x1);
-    swap16(x2, x3);
-    swap32(x0, x2);
-    swap32(x1, x3);
-}
-
 using fp4q_num::bf16_rne_pair;
 
 // Wave-private LDS staging: a wavefront exchanges data among its own lanes
@@ -553,12 +544,16 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     unsigned mw, C[8];
     quantize_groups<kFwht>(R, s, t, mw, C);
 
-    // micro-scales: quarter q holds groups q + 4k; make it groups 4q .. 4q + 3
-    transpose4(t[0], t[1], t[2], t[3]);
-    mw = e4m3_pair<true>(e4m3_pair<false>(0u, t[0], t[1]), t[2], t[3]);
-
     wave_lds_sync();  // every lane has read its chunks from the region
+    // micro-scales: byte k of the quarter-q lane's mw is group q + 4k; its bytes
+    // go to their places in the block's 16 bytes after the code staging (chunk
+    // 144 + p), and the lane reads back groups 4q .. 4q + 3 once store_codes
+    // has synchronised the region
+    unsigned char *mb = reinterpret_cast<unsigned char *>(lds + 144 + L.p) + L.q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mb[4 * k] = (unsigned char)(mw >> (8 * k));
     store_codes<true>(L, nblocks, lds, codes, C);
+    mw = reinterpret_cast<const unsigned *>(lds + 144 + L.p)[L.q];
     if (L.valid) {
         TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, mw);
         if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, as_u(s));
