@@ -8,9 +8,10 @@ step i decompresses the payload compressed in step i-1, so no read is served
 from the 256 MB last-level cache.  Inputs are resident in HBM before the timed
 region.  Prints one JSON line on stdout; progress goes to stderr.
 
-Order of a run: the other GPU legs first (entry-point variants, cold launches,
-the receiver kernels, the transform trade-off, the copy ceiling, the error
-report), which also bring the GPU to a steady state; then W warm-up steps; then
+Order of a run: a quarter second of untimed steps, then the other GPU legs
+(entry-point variants, cold launches, the receiver kernels, the transform
+trade-off, the traffic twins, the copy ceiling, the error report), which also
+bring the GPU to a steady state; then W warm-up steps; then
 K timed steps by wall clock between two synchronisations, with nothing else
 queued in between; then a separate per-kernel pass of KERNEL_PASS steps with
 HIP events around each kernel; then the CPU baseline.
@@ -424,6 +425,18 @@ def receiver_timing(fp4q, inputs, torch, dev, iters: int = 40):
     res["workload"] = ("k=8 peers of bf16 4096x11008 N(0,1e-3), seeds 4..11; the _local entry sums "
                        "peers 0..6 and adds peer 7's bf16 tensor uncompressed")
     return res
+
+
+def spin_up(torch, step, seconds: float = 0.25):
+    """Untimed steps for a fixed wall time before the first measured leg, so that
+    the first leg does not run while the GPU's clocks are still rising."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
 
 
 def variant_timing(fp4q, torch, X, P, Y, iters: int = 40):
@@ -964,6 +977,7 @@ def main():
     # --warmup is.
     result = {}
     if wl == HEADLINE:
+        spin_up(torch, step)
         result["variants"] = variant_timing(fp4q, torch, X, P, Y)
         result["cold"] = cold_timing(fp4q, torch, X, P, Y)
         if not args.no_receiver:
@@ -1005,8 +1019,8 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         t_c, t_d = kernel_pass(fp4q, torch, X, P, Y, S, args.warmup + K)
-        timing = ("order: variant, cold, receiver, trade-off, copy and error legs first (steady "
-                  "state), then %d warm-up steps, then %d timed steps by wall clock (eager launches, "
+        timing = ("order: 0.25 s of untimed steps, then the variant, cold, receiver, trade-off, "
+                  "copy and error legs (steady state), then %d warm-up steps, then %d timed steps by wall clock (eager launches, "
                   "nothing else queued), then a separate pass of %d steps with HIP events around "
                   "each kernel; per-kernel figures are that pass's medians" % (args.warmup, K, KERNEL_PASS))
     log("timed %d steps: %.4f ms/step; per-kernel medians: compress %.1f us, decompress %.1f us "
