@@ -560,13 +560,48 @@ def ceilings(fp4q, inputs, torch, dev, X, P, Y, iters: int = 40):
                      "frac": round(gbps / PEAK_GBPS, 4)}
         log("ceiling %-14s median %7.1f us  %7.1f GB/s  %.1f%% of HBM peak" % (
             name, med * 1e6, gbps, 100 * gbps / PEAK_GBPS))
+    # the twins of the step itself, in the step's context: compress twin and
+    # decompress twin alternated over the same rotation (decompress reading the
+    # previous step's payload), first 20 steps by wall clock, then 60 steps with
+    # events around each launch, as the headline kernels are timed
+    def twin_step(i, e=None):
+        s_ = i % S
+        if e:
+            e[0].record()
+        cases[0][1](s_)
+        if e:
+            e[1].record()
+            e[2].record()
+        ok(L.twin_decompress(*[ptr(t) for t in P[(s_ - 1) % S]], rows, Lr, ptr(Y[s_]), 0, stream()))
+        if e:
+            e[3].record()
+    for i in range(10):
+        twin_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(20):
+        twin_step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / 20
+    ev = [[TimingEvent() for _ in range(4)] for _ in range(KERNEL_PASS)]
+    for i in range(KERNEL_PASS):
+        twin_step(i, ev[i])
+    torch.cuda.synchronize()
+    tc = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    td = float(np.median([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
+    res["step"] = {"ms_per_step": round(wall * 1e3, 4), "compress_median_us": round(tc * 1e6, 2),
+                   "decompress_median_us": round(td * 1e6, 2)}
+    log("ceiling step (twins alternated as the step): %.4f ms/step; per-kernel medians: compress %.1f us, "
+        "decompress %.1f us" % (wall * 1e3, tc * 1e6, td * 1e6))
     del pays, psets, raccs, big, sink
     # the twins wrote the step's payloads and outputs: restore the payloads
     for s_ in range(S):
         fp4q.fp4q_compress(X[s_], *P[s_])
     torch.cuda.synchronize()
     res["what"] = ("compute-free kernels with each kernel's launch shape and memory instructions "
-                   "(tests/hip/fp4q_twins.hip); read/write: plain 512 MiB streams")
+                   "(tests/hip/fp4q_twins.hip), each timed alone; step: the compress and decompress "
+                   "twins alternated as the step alternates the kernels; read/write: plain 512 MiB "
+                   "streams")
     return res
 
 

@@ -145,21 +145,25 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
-// Global stores.  Every kernel writes through buffer stores with the
-// system-scope cache policy (sc1): on MI355X they wrote streaming output about
-// 20 % faster than non-temporal global stores (6.1 against 4.9 TB/s on the
-// decompress traffic pattern, 6.95 against 6.5 on the compress pattern).  A
+// Global stores.  Every kernel writes through buffer stores, by default with
+// the system-scope cache policy (sc1): on MI355X they wrote streaming output
+// about 20 % faster than non-temporal global stores (6.1 against 4.9 TB/s on
+// the decompress traffic pattern, 6.95 against 6.5 on the compress pattern).
+// The k-peer reduce, whose eight read streams share the memory system with its
+// one write stream, writes faster with the non-temporal policy instead.  A
 // wavefront's descriptor covers exactly its tile's part of one output array:
 // the bytes of its valid blocks, none for a wavefront whose tile lies past the
 // last block (the last workgroup of a launch can hold such wavefronts), so a
 // store past the end would also be dropped by the hardware range check; the
 // kernels issue none.
-constexpr int kStorePolicy = 16;  // sc1
-struct TileStore {
+constexpr int kStoreSc1 = 16;
+constexpr int kStoreNt = 2;
+template <int kPolicy>
+struct TileStoreP {
     __amdgpu_buffer_rsrc_t r;
     // bytes_per_block of the array, for the tile's blocks [tile, tile + tile_blocks) that exist
-    __device__ __forceinline__ TileStore(void *base, int64_t tile, int64_t nblocks,
-                                         int bytes_per_block, int tile_blocks = kTileBlocks) {
+    __device__ __forceinline__ TileStoreP(void *base, int64_t tile, int64_t nblocks,
+                                          int bytes_per_block, int tile_blocks = kTileBlocks) {
         const int64_t left = nblocks - tile;
         const int64_t nvalid = left < 0 ? 0 : left < tile_blocks ? left : tile_blocks;
         r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(base) + tile * bytes_per_block, 0,
@@ -167,18 +171,31 @@ struct TileStore {
     }
     __device__ __forceinline__ void b128(int byte_offset, uint4 v) const {
         const u32x4 t = {v.x, v.y, v.z, v.w};
-        __builtin_amdgcn_raw_buffer_store_b128(t, r, byte_offset, 0, kStorePolicy);
+        __builtin_amdgcn_raw_buffer_store_b128(t, r, byte_offset, 0, kPolicy);
     }
     __device__ __forceinline__ void b32(int byte_offset, unsigned v) const {
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_offset, 0, kStorePolicy);
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_offset, 0, kPolicy);
     }
     __device__ __forceinline__ void b16(int byte_offset, unsigned short v) const {
-        __builtin_amdgcn_raw_buffer_store_b16(v, r, byte_offset, 0, kStorePolicy);
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, byte_offset, 0, kPolicy);
     }
     __device__ __forceinline__ void b8(int byte_offset, unsigned char v) const {
-        __builtin_amdgcn_raw_buffer_store_b8(v, r, byte_offset, 0, kStorePolicy);
+        __builtin_amdgcn_raw_buffer_store_b8(v, r, byte_offset, 0, kPolicy);
     }
 };
+#ifndef FP4Q_REDUCE_STORE_POLICY
+#define FP4Q_REDUCE_STORE_POLICY kStoreNt
+#endif
+using TileStore = TileStoreP<kStoreSc1>;                     // scales: a few bytes per lane
+using ReduceStore = TileStoreP<FP4Q_REDUCE_STORE_POLICY>;    // the k-peer reduce's output
+// Codes and outputs (1 KiB per instruction): the transform kernels of the hot
+// path write them with sc1 and the non-temporal policy together, the other
+// kernels with sc1 alone (each the faster in its own steady state; a single
+// launch on an idle GPU reads faster with sc1 alone, whose writes the
+// last-level cache absorbs and drains after the kernel has ended).
+constexpr int kStoreSc1Nt = kStoreSc1 | kStoreNt;
+template <bool kHotTransform>
+constexpr int kStreamPolicy = kHotTransform ? kStoreSc1Nt : kStoreSc1;
 
 // A buffer descriptor over the wavefront's tile of an array with
 // bytes_per_block bytes per block: the bytes of the tile's nvalid existing
@@ -454,7 +471,7 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
 //     elements 16 q + 64 (w >> 1) + 8 (w & 1) ..): C[w] is dword
 //     2 q + 8 (w >> 1) + (w & 1) of the block, so C[2 m], C[2 m + 1] is one
 //     8-byte write (chunk (q >> 1) + 2 m, dwords 2 (q & 1), + 1).
-template <bool kGroups>
+template <bool kGroups, int kPolicy = kStoreSc1>
 __device__ __forceinline__ void store_codes(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
                                             uint4 *__restrict__ codes, const unsigned (&C)[8]) {
     const int lane = L.lane;
@@ -468,7 +485,7 @@ __device__ __forceinline__ void store_codes(const Lane &L, int64_t nblocks, uint
     }
     wave_lds_sync();
     const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
-    const TileStore out(codes, L.tile, nblocks, 128);
+    const TileStoreP<kPolicy> out(codes, L.tile, nblocks, 128);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int b = 8 * u + (lane >> 3);  // block within the tile
@@ -552,7 +569,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     unsigned char *mb = reinterpret_cast<unsigned char *>(lds + 144 + L.p) + L.q;
 #pragma unroll
     for (int k = 0; k < 4; ++k) mb[4 * k] = (unsigned char)(mw >> (8 * k));
-    store_codes<true>(L, nblocks, lds, codes, C);
+    store_codes<true, kStreamPolicy<kFwht>>(L, nblocks, lds, codes, C);
     mw = reinterpret_cast<const unsigned *>(lds + 144 + L.p)[L.q];
     if (L.valid) {
         TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, mw);
@@ -723,7 +740,7 @@ __device__ __forceinline__ bool fold_sixteenth(float block_scale) {
 // that each global store instruction writes 1 KiB of contiguous output (64
 // lanes x 16 bytes), the pattern the memory system absorbs fastest (stores with
 // the sc1 policy, TileStore).
-template <bool kBf16>
+template <bool kBf16, int kPolicy = kStoreSc1>
 __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
                                           void *__restrict__ out, const float (&R)[64]) {
     const int lane = L.lane, p = L.p;
@@ -740,7 +757,7 @@ __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 
         }
         wave_lds_sync();
         const uint4 *src = lds + 33 * (lane >> 5) + (lane & 31);
-        const TileStore dst_g(out, tile, nblocks, 512);
+        const TileStoreP<kPolicy> dst_g(out, tile, nblocks, 512);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {  // blocks 2u, 2u + 1 of the tile
             const int b = 2 * u + (lane >> 5);
@@ -751,7 +768,7 @@ __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 
         // a block is 64 chunks of 4 fp32 (stride 65); register quad v holds chunk
         // q + 8 (v & 1) + 16 (v >> 1 & 1) + 4 (v >> 2 & 1) + 32 (v >> 3).
         // Rounds of kRoundBlocks blocks each.
-        const TileStore dst_g(out, tile, nblocks, 1024);
+        const TileStoreP<kPolicy> dst_g(out, tile, nblocks, 1024);
 #pragma unroll
         for (int h = 0; h < kTileBlocks / kRoundBlocks; ++h) {
             if (p / kRoundBlocks == h) {
@@ -788,7 +805,7 @@ __global__ __launch_bounds__(kWave * kDecompressWaves<kBf16>) void decompress_ke
     const bool fold = kFwht && fold_sixteenth(P.s);
     dequant<kSet>(P, R, fold ? 0.0625f : 1.0f);
     receiver_transform<kFwht, kBf16>(L, wl, R, fold);
-    store_out<kBf16>(L, nblocks, wl, out, R);
+    store_out<kBf16, kStreamPolicy<kFwht>>(L, nblocks, wl, out, R);
 }
 
 // --------------------------------------------------- receiver-side reduce
@@ -1129,7 +1146,7 @@ __device__ __forceinline__ void narrow_store_out(const NarrowLane &L, int64_t nb
             }
         wave_lds_sync();
         const uint4 *src = lds + 33 * (lane >> 5) + (lane & 31);
-        const TileStore dst_g(out, L.tile, nblocks, 512, kNarrowBlocks);
+        const ReduceStore dst_g(out, L.tile, nblocks, 512, kNarrowBlocks);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {  // blocks 2u, 2u + 1
             const int b = 2 * u + (lane >> 5);
@@ -1139,7 +1156,7 @@ __device__ __forceinline__ void narrow_store_out(const NarrowLane &L, int64_t nb
     } else {
         // a block is 64 chunks of 4 fp32 (stride 65); run h is chunks 32 h + 4 f .. + 3;
         // two rounds of four blocks
-        const TileStore dst_g(out, L.tile, nblocks, 1024, kNarrowBlocks);
+        const ReduceStore dst_g(out, L.tile, nblocks, 1024, kNarrowBlocks);
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
             if ((p >> 2) == rd) {

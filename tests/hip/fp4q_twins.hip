@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kWave * kDecompressWaves<kBf16>) void twin_decompre
     const unsigned w[8] = {P.c0.x, P.c0.y, P.c0.z, P.c0.w, P.c1.x, P.c1.y, P.c1.z, P.c1.w};
     float R[64];
     fill_registers(w, P.lo ^ P.hi ^ as_u(P.s), R);
-    store_out<kBf16>(L, nblocks, wl, out, R);
+    store_out<kBf16, kStreamPolicy<true>>(L, nblocks, wl, out, R);
 }
 
 // accumulate_narrow_kernel<true, false>'s traffic: k payloads loaded as the
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void twin_compress_kernel(
         C[i] = x.x ^ x.y ^ x.z ^ x.w;
     }
     wave_lds_sync();  // every lane has read its chunks from the region
-    store_codes<true>(L, nblocks, lds, codes, C);
+    store_codes<true, kStreamPolicy<true>>(L, nblocks, lds, codes, C);
     if (L.valid) {
         TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, C[0] ^ C[5]);
         if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, C[1] ^ C[7]);
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void twin_write_kernel(uint4 *__restrict__ out
     const int64_t wv = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
     if (wv >= nwaves) return;
     const int lane = threadIdx.x & (kWave - 1);
-    const TileStore dst(out + wv * 1024, 0, 1, 16384, 1);
+    const TileStoreP<kStreamPolicy<true>> dst(out + wv * 1024, 0, 1, 16384, 1);
 #pragma unroll
     for (int j = 0; j < 16; ++j) dst.b128(16 * (64 * j + lane), make_uint4(lane, j, 0, 0));
 }
