@@ -738,8 +738,8 @@ __device__ __forceinline__ bool fold_sixteenth(float block_scale) {
 
 // Output staging: every lane's values go through the wave-private LDS region so
 // that each global store instruction writes 1 KiB of contiguous output (64
-// lanes x 16 bytes), the pattern the memory system absorbs fastest (stores with
-// the sc1 policy, TileStore).
+// lanes x 16 bytes), the pattern the memory system absorbs fastest; kPolicy is
+// the stores' cache policy.
 template <bool kBf16, int kPolicy = kStoreSc1>
 __device__ __forceinline__ void store_out(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
                                           void *__restrict__ out, const float (&R)[64]) {
