@@ -590,13 +590,20 @@ def test_random_sweep(fp4q, chunk):
                     for r in (oracle.compress(p, fwht=fwht) for p in peers)]
             dev_trip = [tuple(to_dev(a) for a in t) for t in trip]
             acc = fp4q.fp4q_decompress_accumulate(dev_trip, flags=flags)
+            accb = fp4q.fp4q_decompress_accumulate(dev_trip, out_dtype=torch.bfloat16, flags=flags)
             req = fp4q.fp4q_reduce_requantize(dev_trip, local=to_dev(xb), flags=flags)
+            req0 = fp4q.fp4q_reduce_requantize(dev_trip, flags=flags)
             torch.cuda.synchronize()
             # the peers' rows carry unrelated scales (2^-30 .. 2^30), so their terms can
             # cancel: the reduce is held to 1e-6 of the summed term magnitudes
             mag = sum(np.abs(oracle.decompress_f64(*t, fwht=fwht)) for t in trip)
             parity.check_rowwise(acc.cpu().numpy(), oracle.accumulate_f64(trip, fwht=fwht),
                                  magnitude=mag)
+            # the bf16 output is the bf16 rounding of the same fp32 sum, bit for bit
+            np.testing.assert_array_equal(accb.cpu().view(torch.int16).numpy().view(np.uint16),
+                                          oracle.round_bf16(acc.cpu().numpy()))
             parity.check_compress_exact([o.cpu().numpy() for o in req],
                                         oracle.requantize(trip, debug=True, local=xb, fwht=fwht))
+            parity.check_compress_exact([o.cpu().numpy() for o in req0],
+                                        oracle.requantize(trip, debug=True, fwht=fwht))
     _say("  sweep chunk %d: every payload byte exact" % chunk)
