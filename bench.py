@@ -900,6 +900,50 @@ def graph_timed_steps(torch, fp4q, step, X, P, Y, S, args, min_steps: int = 40):
     return args.steps, wall, per["compress"], per["decompress"], timing
 
 
+SWEEP_ROWS = (64, 512, 1024, 2048, 4096, 8192)
+
+
+def size_sweep(fp4q, torch, dev, launches: int = 40, replays: int = 7):
+    """Launch time against tensor size (rows of 4096, N(0,1), seed 5): for each
+    size a HIP graph of `launches` compress (then decompress) calls on the same
+    buffers, replayed `replays` times with events around each replay; the median
+    replay divided by `launches`.  The small tensors stay in the caches: this
+    measures the fixed cost of a launch and its ramp, not HBM rates."""
+    out = []
+    for rows in SWEEP_ROWS:
+        x = torch.from_numpy(np.random.default_rng(5).standard_normal((rows, 4096), dtype=np.float32)).to(dev)
+        x = x.to(torch.bfloat16)
+        P = fp4q.fp4q_compress(x)
+        y = torch.empty((rows, 4096), dtype=torch.float32, device=dev)
+        calls = {"compress": lambda: fp4q.fp4q_compress(x, *P),
+                 "decompress": lambda: fp4q.fp4q_decompress(*P, out=y)}
+        row = {"rows": rows, "wavefronts": rows * 4096 // 256 // 16}
+        for name, call in calls.items():
+            s = torch.cuda.Stream()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    call()
+                s.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    for _ in range(launches):
+                        call()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(replays):
+                a, b = TimingEvent(), TimingEvent()
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / launches)
+            row[name + "_us"] = round(float(np.median(ts)), 2)
+        log("size %5d rows (%5d wavefronts): compress %6.2f us, decompress %6.2f us" % (
+            rows, row["wavefronts"], row["compress_us"], row["decompress_us"]))
+        out.append(row)
+    return out
+
+
 def kernel_pass(fp4q, torch, X, P, Y, S, first_step: int, steps: int = KERNEL_PASS):
     """Per-kernel durations, in a pass of its own after the timed region: `steps`
     more steps of the same rotation, each kernel bracketed by its own pair of
@@ -949,6 +993,8 @@ def main():
                     help="skip timing the compute-free traffic twins of the kernels")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain %d-byte device copy (counter scale reference)" % COPY_REF_BYTES)
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="only time compress and decompress launches against tensor size (rows of 4096)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--timed-steps", type=int, default=0,
@@ -985,6 +1031,9 @@ def main():
         if args.copy_reference:
             copy_reference(torch, dev)
         print(json.dumps({"receiver": receiver_timing(fp4q, inputs, torch, dev)}), flush=True)
+        return
+    if args.size_sweep:
+        print(json.dumps({"size_sweep": size_sweep(fp4q, torch, dev)}), flush=True)
         return
     wl = args.workload
     rows, L = inputs.CONFIGS[wl][:2]

@@ -193,9 +193,13 @@ using ReduceStore = TileStoreP<FP4Q_REDUCE_STORE_POLICY>;    // the k-peer reduc
 // kernels with sc1 alone (each the faster in its own steady state; a single
 // launch on an idle GPU reads faster with sc1 alone, whose writes the
 // last-level cache absorbs and drains after the kernel has ended).
-constexpr int kStoreSc1Nt = kStoreSc1 | kStoreNt;
+// A build for a pipeline that runs other work between the kernels can give the
+// transform kernels sc1 alone (-DFP4Q_HOT_STREAM_POLICY=16).
+#ifndef FP4Q_HOT_STREAM_POLICY
+#define FP4Q_HOT_STREAM_POLICY (kStoreSc1 | kStoreNt)
+#endif
 template <bool kHotTransform>
-constexpr int kStreamPolicy = kHotTransform ? kStoreSc1Nt : kStoreSc1;
+constexpr int kStreamPolicy = kHotTransform ? FP4Q_HOT_STREAM_POLICY : kStoreSc1;
 
 // A buffer descriptor over the wavefront's tile of an array with
 // bytes_per_block bytes per block: the bytes of the tile's nvalid existing
