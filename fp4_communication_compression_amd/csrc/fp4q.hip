@@ -469,24 +469,18 @@ __device__ __forceinline__ void quantize_groups(const float (&R)[64], float &s, 
 
 // Codes of a tile through LDS (8 chunks per block, stride 9); the tile's 2 KiB
 // of codes then leave in two 1 KiB stores.  The caller has finished any earlier
-// use of the LDS region.  Where the lane's eight code dwords go:
-//   kGroups = false: C[0..3] is the 16-byte chunk q of its block, C[4..7] chunk q + 4;
-//   kGroups = true (the compress layout, dword w = registers 8 w .. 8 w + 7 =
-//     elements 16 q + 64 (w >> 1) + 8 (w & 1) ..): C[w] is dword
-//     2 q + 8 (w >> 1) + (w & 1) of the block, so C[2 m], C[2 m + 1] is one
-//     8-byte write (chunk (q >> 1) + 2 m, dwords 2 (q & 1), + 1).
-template <bool kGroups, int kPolicy = kStoreSc1>
+// use of the LDS region.  The lane's eight code dwords are in the quantisation
+// layout (dword w = registers 8 w .. 8 w + 7 = elements 16 q + 64 (w >> 1) +
+// 8 (w & 1) ..): C[w] is dword 2 q + 8 (w >> 1) + (w & 1) of the block, so
+// C[2 m], C[2 m + 1] is one 8-byte write (chunk (q >> 1) + 2 m, dwords 2 (q & 1),
+// + 1).
+template <int kPolicy = kStoreSc1>
 __device__ __forceinline__ void store_codes(const Lane &L, int64_t nblocks, uint4 *__restrict__ lds,
                                             uint4 *__restrict__ codes, const unsigned (&C)[8]) {
     const int lane = L.lane;
-    if constexpr (kGroups) {
-        uint2 *dst = reinterpret_cast<uint2 *>(lds + 9 * L.p + (L.q >> 1)) + (L.q & 1);
+    uint2 *dst = reinterpret_cast<uint2 *>(lds + 9 * L.p + (L.q >> 1)) + (L.q & 1);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) dst[4 * m] = make_uint2(C[2 * m], C[2 * m + 1]);
-    } else {
-        lds[9 * L.p + L.q] = make_uint4(C[0], C[1], C[2], C[3]);
-        lds[9 * L.p + L.q + 4] = make_uint4(C[4], C[5], C[6], C[7]);
-    }
+    for (int m = 0; m < 4; ++m) dst[4 * m] = make_uint2(C[2 * m], C[2 * m + 1]);
     wave_lds_sync();
     const uint4 *srcl = lds + 9 * (lane >> 3) + (lane & 7);
     const TileStoreP<kPolicy> out(codes, L.tile, nblocks, 128);
@@ -573,7 +567,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
     unsigned char *mb = reinterpret_cast<unsigned char *>(lds + 144 + L.p) + L.q;
 #pragma unroll
     for (int k = 0; k < 4; ++k) mb[4 * k] = (unsigned char)(mw >> (8 * k));
-    store_codes<true, kStreamPolicy<kFwht>>(L, nblocks, lds, codes, C);
+    store_codes<kStreamPolicy<kFwht>>(L, nblocks, lds, codes, C);
     mw = reinterpret_cast<const unsigned *>(lds + 144 + L.p)[L.q];
     if (L.valid) {
         TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, mw);
@@ -585,15 +579,18 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_kernel(
 // Code layout in the lane: chunks q and q + 4 of its block (16 bytes = 32 codes
 // each).  Decompress loads them so, instruction h of quarter q reading chunk
 // q + 4 h: the four quarters read 64 contiguous bytes per instruction.  The
-// multi-peer kernels instead read each peer's 2 KiB of tile codes as two
-// contiguous 1 KiB loads and re-deal them through LDS (redeal_codes): 3 % faster
-// over 8 peers, but 7 % slower for decompress's single payload, whose one load
-// round then carries the LDS round trip on its critical path.
+// re-quantisation with a local slice instead reads each peer's 2 KiB of tile
+// codes as two contiguous 1 KiB loads and re-deals them through LDS
+// (redeal_group_codes), into its own layout; for decompress's single payload
+// that LDS round trip measured 7 % slower, on its one load round's critical path.
 // Register j = 32 h + 8 w + t holds element 32 q + 128 h + 8 w + t: register
 // bits 0-4 = index bits 0-4, bit 5 = index bit 7; lane bits 4, 5 = index bits
 // 5, 6.  Its micro-group is (j >> 4 & 1) + 2 q + 8 h, so register group j >> 4
 // uses micro byte 2 q + (j >> 4 & 1) + 8 (j >> 5).
 // One lane's part of a payload: 32 code bytes, two micro-scale pairs, the block scale.
+// (The re-quantisation's grouped layout keeps the same fields: dwords 2 k,
+// 2 k + 1 of c0, c1 hold micro-group q + 4 k, lo and hi its bytes q, q + 4 and
+// q + 8, q + 12.)
 struct PayloadRegs {
     uint4 c0, c1;
     unsigned lo, hi;  // micro-scale bytes (2q, 2q + 1) and (2q + 8, 2q + 9) in the low halves
@@ -617,11 +614,14 @@ __device__ __forceinline__ PayloadRegs load_payload(const Lane &L, const uint4 *
     return P;
 }
 
-// A peer's payload for the multi-peer kernels, through buffer descriptors over
-// the wavefront's tile: codes in the contiguous order (tile chunk 64 j + lane,
-// chunk lane & 7 of block 8 j + (lane >> 3); redeal_codes gives the lane
-// layout), the lane's two micro-scale pairs as 2-byte loads, the block scale.
-// Lanes of blocks past the end read zeros and never store.
+// A peer's payload for the re-quantisation with a local slice, which sums in
+// compress's quantisation layout (register 16 k + i = element 16 q + 64 k + i,
+// micro-group q + 4 k), through buffer descriptors over the wavefront's tile:
+// codes in the contiguous order (tile chunk 64 j + lane, chunk lane & 7 of
+// block 8 j + (lane >> 3); redeal_group_codes gives the lane its groups), the
+// block's 16 micro-scale bytes in one load, of which the lane keeps bytes q and
+// q + 4 (lo) and q + 8 and q + 12 (hi), and the block scale.  Lanes of blocks
+// past the end read zeros and never store.
 __device__ __forceinline__ PayloadRegs load_payload_tile(const Lane &L, int64_t nblocks,
                                                          const uint4 *__restrict__ codes,
                                                          const uint4 *__restrict__ micro,
@@ -634,25 +634,31 @@ __device__ __forceinline__ PayloadRegs load_payload_tile(const Lane &L, int64_t 
     const u32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(rc, 1024 + 16 * L.lane, 0, kLoadNt);
     P.c0 = make_uint4(c0[0], c0[1], c0[2], c0[3]);
     P.c1 = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-    P.lo = __builtin_amdgcn_raw_buffer_load_b16(rm, 16 * L.p + 2 * L.q, 0, 0);
-    P.hi = __builtin_amdgcn_raw_buffer_load_b16(rm, 16 * L.p + 8 + 2 * L.q, 0, 0);
+    const u32x4 m = __builtin_amdgcn_raw_buffer_load_b128(rm, 16 * L.p, 0, 0);
+    // byte q of dwords x, y (then z, w) into bytes 0, 1 (perm: selectors 0-3 pick
+    // the second operand's bytes, 4-7 the first's)
+    const unsigned sel = (unsigned)L.q | ((unsigned)(L.q + 4) << 8);
+    P.lo = __builtin_amdgcn_perm(m[1], m[0], sel);
+    P.hi = __builtin_amdgcn_perm(m[3], m[2], sel);
     P.s = as_f(__builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(block, L.tile, nvalid, 4), 4 * L.p, 0, 0));
     return P;
 }
 
-// Contiguously loaded codes to the lane layout through the wavefront's LDS
-// region (at least 144 chunks, free): tile chunk c goes to chunk 9 (c >> 3) +
-// (c & 7) (a padding chunk per block keeps the reads free of bank conflicts),
-// and lane (p, q) reads chunks q and q + 4 of block p.
-__device__ __forceinline__ void redeal_codes(const Lane &L, uint4 *__restrict__ lds, PayloadRegs &P) {
+// Contiguously loaded codes to the quantisation layout through the wavefront's
+// LDS region (at least 144 chunks, free): tile chunk c goes to chunk
+// 9 (c >> 3) + (c & 7) (a padding chunk per block), and lane (p, q) reads the
+// 8 bytes of each of its groups q + 4 k, half q & 1 of chunk (q >> 1) + 2 k of
+// block p: dwords 2 k, 2 k + 1 of c0, c1.
+__device__ __forceinline__ void redeal_group_codes(const Lane &L, uint4 *__restrict__ lds, PayloadRegs &P) {
     wave_lds_sync();  // earlier reads of the region are done
     uint4 *w = lds + 9 * (L.lane >> 3) + (L.lane & 7);
     w[0] = P.c0;
     w[72] = P.c1;
     wave_lds_sync();
-    const uint4 *r = lds + 9 * L.p + L.q;
-    P.c0 = r[0];
-    P.c1 = r[4];
+    const uint2 *r = reinterpret_cast<const uint2 *>(lds + 9 * L.p + (L.q >> 1)) + (L.q & 1);
+    const uint2 g0 = r[0], g1 = r[4], g2 = r[8], g3 = r[12];
+    P.c0 = make_uint4(g0.x, g0.y, g1.x, g1.y);
+    P.c1 = make_uint4(g2.x, g2.y, g3.x, g3.y);
 }
 
 // Registers j = 0..63 get E2M1(code) * S_g (kSet), or the product is added to
@@ -865,7 +871,7 @@ __device__ __forceinline__ void sum_peers(const Lane &L, int64_t nblocks, const 
     for_each_peer(
         k, [&](int p) { return load_payload_tile(L, nblocks, peers.codes[p], peers.micro[p], peers.block[p]); },
         [&](PayloadRegs &P, auto) {
-            redeal_codes(L, lds, P);
+            redeal_group_codes(L, lds, P);
             dequant<kAdd>(P, R);
         });
 }
@@ -878,57 +884,40 @@ __device__ __forceinline__ void sum_peers(const Lane &L, int64_t nblocks, const 
 // inverse transform is needed, since decompressing, summing and compressing
 // would apply the self-inverse H / 16 twice.  With the rank's own uncompressed
 // part of the slice (this kernel), the accumulator starts at that part,
-// transformed as compress transforms its input; without one it starts at +0
+// transformed exactly as compress transforms its input (its loads, its
+// transform with the lane exchange through LDS, then the 1/16, exact for
+// bfloat16 inputs), so the sum lives in compress's quantisation layout and
+// leaves through compress's epilogue; without a local slice it starts at +0
 // (requantize_narrow_kernel below).
-// Register j of quarter q holds element 32 q + 128 (j >> 5) + (j & 31), so
-// register group k = j >> 4 is micro-group (k & 1) + 2 q + 8 (k >> 1), and code
-// dwords 0-3 / 4-7 are the block's 16-byte chunks q / q + 4.
-// The local tile arrives as register j = element 64 q + j (index bits 0-5 in
-// the register, 6 and 7 in lane bits 4 and 5); butterflies on index bits 0-5,
-// then two exchanges through register bit 5 bring index bit 6 in (and 5 out to
-// lane bit 4), then bit 7 in (and 6 out to lane bit 5): the layout above, with
-// the butterflies in ascending index-bit order.
-template <bool kFwht>
-__device__ __forceinline__ void local_transform(float (&R)[64]) {
-    if constexpr (kFwht) {
-        stage<1>(R);
-        stage<2>(R);
-        stage<4>(R);
-        stage<8>(R);
-        stage<16>(R);
-        stage<32>(R);
-    }
-    swap_lane4<32>(R);
-    if constexpr (kFwht) stage<32>(R);  // index bit 6
-    swap_lane5<32>(R);
-    if constexpr (kFwht) {
-        stage<32>(R);  // index bit 7
-#pragma unroll
-        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
-    }
-}
-
 template <bool kFwht>
 __global__ __launch_bounds__(kWave * kReceiverWaves) void requantize_kernel(
     Peers peers, int k, const uint4 *__restrict__ local, int64_t nblocks,
-    uint4 *__restrict__ codes, unsigned short *__restrict__ micro, float *__restrict__ block) {
+    uint4 *__restrict__ codes, unsigned *__restrict__ micro, float *__restrict__ block) {
     __shared__ uint4 lds_all[kReceiverWaves * kStageChunks];
     const Lane L = lane_map<kReceiverWaves>(nblocks);
     uint4 *lds = lds_all + (threadIdx.x / kWave) * kStageChunks;
     float R[64];
-    load_widen<false>(L, local, nblocks, lds, R);
-    local_transform<kFwht>(R);
-    wave_lds_sync();  // every lane has read its input chunks
+    load_widen<!kFwht>(L, local, nblocks, lds, R);
+    compress_transform<kFwht>(L, lds, R);
+    if constexpr (kFwht) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) R[j] *= 0.0625f;
+    }
+    wave_lds_sync();  // every lane has read its chunks from the region
     sum_peers(L, nblocks, peers, k, lds, R);
 
     float s, t[4];
     unsigned mw, C[8];
     quantize_groups<false>(R, s, t, mw, C);
-    store_codes<false>(L, nblocks, lds, codes, C);
+    wave_lds_sync();  // every lane has read its re-dealt codes
+    // micro-scales to their stored order through the region, as compress does
+    unsigned char *mb = reinterpret_cast<unsigned char *>(lds + 144 + L.p) + L.q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) mb[4 * g] = (unsigned char)(mw >> (8 * g));
+    store_codes(L, nblocks, lds, codes, C);
+    mw = reinterpret_cast<const unsigned *>(lds + 144 + L.p)[L.q];
     if (L.valid) {
-        const TileStore m(micro, L.tile, nblocks, 16);
-        m.b16(16 * L.p + 2 * L.q, (unsigned short)(mw & 0xFFFFu));      // groups 2q, 2q + 1
-        m.b16(16 * L.p + 8 + 2 * L.q, (unsigned short)(mw >> 16));      // groups 2q + 8, 2q + 9
+        TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, mw);
         if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, as_u(s));
     }
 }
@@ -1264,7 +1253,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void compress_mx_kernel(
         C[w] = c;
     }
     wave_lds_sync();  // every lane has read its chunks from the region
-    store_codes<true>(L, nblocks, lds, codes, C);
+    store_codes(L, nblocks, lds, codes, C);
     if (L.valid && (q & 1) == 0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)

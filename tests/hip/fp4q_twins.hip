@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kWave * kSenderWaves) void twin_compress_kernel(
         C[i] = x.x ^ x.y ^ x.z ^ x.w;
     }
     wave_lds_sync();  // every lane has read its chunks from the region
-    store_codes<true, kStreamPolicy<true>>(L, nblocks, lds, codes, C);
+    store_codes<kStreamPolicy<true>>(L, nblocks, lds, codes, C);
     if (L.valid) {
         TileStore(micro, L.tile, nblocks, 16).b32(16 * L.p + 4 * L.q, C[0] ^ C[5]);
         if (L.q == 0) TileStore(block, L.tile, nblocks, 4).b32(4 * L.p, C[1] ^ C[7]);
