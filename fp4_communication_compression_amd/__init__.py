@@ -42,11 +42,16 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded C library (raises if it has not been built)."""
+    """The loaded C library, built first (hipcc, gfx950) if it is not there yet;
+    raises if it can be neither found nor built.  There is no other path."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError("fp4q: %s is missing; build it with __graft_entry__.build()" % LIB_PATH)
+            from . import _build
+            try:
+                _build.build(force=False)
+            except Exception as e:  # noqa: BLE001 - reported with the cause
+                raise ImportError("fp4q: %s is missing and could not be built: %s" % (LIB_PATH, e)) from e
         L = ctypes.CDLL(LIB_PATH)
         P, I, I64, U32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
         PP = ctypes.POINTER(ctypes.c_void_p)

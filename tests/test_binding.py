@@ -80,3 +80,16 @@ def test_mx_arguments():
     with pytest.raises(ValueError, match="GPU"):
         fp4q.fp4q_decompress_mx(torch.zeros((4, 128), dtype=torch.uint8),
                                 torch.zeros((4, 8), dtype=torch.uint8))
+
+
+def test_missing_library_that_cannot_be_built_fails_loudly(tmp_path, monkeypatch):
+    """No library and no way to build one: the binding raises instead of falling
+    back to anything else."""
+    from fp4_communication_compression_amd import _build
+    missing = str(tmp_path / "libfp4q.so")
+    monkeypatch.setattr(fp4q, "_lib", None)
+    monkeypatch.setattr(fp4q, "LIB_PATH", missing)
+    monkeypatch.setattr(_build, "LIB", missing)
+    monkeypatch.setattr(_build, "HIPCC", "/bin/false")
+    with pytest.raises(ImportError, match="could not be built"):
+        fp4q.lib()
