@@ -32,8 +32,8 @@
 //   * the receiver ends with 16-byte register quads of contiguous output.
 // Otherwise LDS only re-deals data between that lane-local layout and fully
 // coalesced 1 KiB-per-instruction global accesses (the bf16 input tile, the
-// multi-peer kernels' code loads, the codes and the output), in a region
-// private to each wavefront.  No MFMA: the work is streaming and the transform
+// peers' codes of the re-quantisation with a local slice, the codes and the
+// output), in a region private to each wavefront.  No MFMA: the work is streaming and the transform
 // is butterflies.
 //
 // The k-peer kernels whose time is their per-peer arithmetic use a narrow
