@@ -157,12 +157,22 @@ def test_reduce_nofwht_and_bf16(fp4q):
                                   oracle.round_bf16(out32.cpu().numpy()))
 
 
-def test_reduce_full_size(fp4q):
+@pytest.fixture(scope="module")
+def reduce_peers():
+    """The 8 peers of the reduce workload (4096 x 11008, N(0, 1e-3), seeds 4..11)
+    and their oracle payloads, made once for the full-size receiver tests."""
+    peers = [inputs.make_reduce_peer(p) for p in range(8)]
+    trip = [(r["codes"], r["micro"], r["block"]) for r in (oracle.compress(p) for p in peers)]
+    return peers, trip
+
+
+def test_reduce_full_size(fp4q, reduce_peers):
     """k = 8 payloads of 4096 x 11008, N(0, 1e-3), seeds 4..11 -> fp32."""
     _say("reduce full k=8 4096x11008")
-    peers = [inputs.make_reduce_peer(p) for p in range(8)]
-    out, want = _reduce_case(fp4q, peers)
-    worst = parity.check_rowwise(out.cpu().numpy(), want)
+    _, trip = reduce_peers
+    out = fp4q.fp4q_decompress_accumulate([tuple(to_dev(a) for a in t) for t in trip])
+    torch.cuda.synchronize()
+    worst = parity.check_rowwise(out.cpu().numpy(), oracle.accumulate_f64(trip))
     _say("  worst row error / row max = %.3e" % worst)
 
 
@@ -199,16 +209,50 @@ def test_requantize_edge_cases(fp4q, kind):
     parity.check_compress_exact([o.cpu().numpy() for o in out], ref)
 
 
-def test_requantize_full_size(fp4q):
+def test_requantize_full_size(fp4q, reduce_peers):
     """k = 8 slices of 4096 x 11008 (the reduce workload)."""
     _say("requantize full k=8 4096x11008")
-    peers = [inputs.make_reduce_peer(p) for p in range(8)]
-    trip = [(r["codes"], r["micro"], r["block"]) for r in (oracle.compress(p) for p in peers)]
+    _, trip = reduce_peers
     ref = oracle.requantize(trip, debug=True)
     out = fp4q.fp4q_reduce_requantize([tuple(to_dev(a) for a in t) for t in trip])
     torch.cuda.synchronize()
     st = parity.check_compress_exact([o.cpu().numpy() for o in out], ref)
     _say("  %s" % st)
+
+
+def test_max_peers_full_size(fp4q, reduce_peers):
+    """The largest peer count, k = 16, at the receiver's real shape (4096 x
+    11008).  Peers 8..15 are peers 0..7 doubled: their payloads are the oracle's
+    with every block scale doubled, exactly the compress of 2x (scaling by a
+    power of two only moves the block scale), and the local slice of the
+    re-quantisation (15 peers + the 16th peer's tensor) is 2x peer 7 in bf16.
+    The accumulate (fp32 and bf16), the re-quantisation and the re-quantisation
+    with the local slice run over the whole tensors, in the launch configuration
+    the bench times; sampled rows on both sides of every 1024-row boundary, plus
+    random rows, are checked against the oracle on those rows' payload slices
+    (blocks never straddle rows), the bf16 output over the whole tensor."""
+    _say("max peers k=16 4096x11008")
+    peers, trip = reduce_peers
+    trip16 = list(trip) + [(c, m, 2.0 * b) for c, m, b in trip]
+    local = ((peers[7].astype(np.uint32) << 16).view(np.float32) * 2.0).view(np.uint32) >> 16
+    local = local.astype(np.uint16)
+    dev = [tuple(to_dev(a) for a in t) for t in trip16]
+    acc = fp4q.fp4q_decompress_accumulate(dev)
+    accb = fp4q.fp4q_decompress_accumulate(dev, out_dtype=torch.bfloat16)
+    req = fp4q.fp4q_reduce_requantize(dev)
+    reql = fp4q.fp4q_reduce_requantize(dev[:15], local=to_dev(local))
+    torch.cuda.synchronize()
+    acc_h = acc.cpu().numpy()
+    np.testing.assert_array_equal(accb.cpu().view(torch.int16).numpy().view(np.uint16),
+                                  oracle.round_bf16(acc_h))
+    rng = np.random.default_rng(16)
+    rows = sorted(set([0, 1, 4095] + [b + d for b in (1024, 2048, 3072) for d in (-1, 0)] +
+                      rng.integers(0, 4096, 48).tolist()))
+    sl = [tuple(a[rows] for a in t) for t in trip16]
+    parity.check_rowwise(acc_h[rows], oracle.accumulate_f64(sl))
+    parity.check_compress_exact([o.cpu().numpy()[rows] for o in req], oracle.requantize(sl, debug=True))
+    parity.check_compress_exact([o.cpu().numpy()[rows] for o in reql],
+                                oracle.requantize(sl[:15], debug=True, local=local[rows]))
 
 
 def run_mx(fp4q, xb, fwht, name):
@@ -444,12 +488,16 @@ def test_requantize_local_alone_is_compress(fp4q, fwht):
         assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
 
 
-def test_requantize_local_full_size(fp4q):
+def test_requantize_local_full_size(fp4q, reduce_peers):
     """An 8-rank slice: 7 received payloads of 4096 x 11008 plus the rank's own
     uncompressed part (the eighth tensor of the reduce workload)."""
-    peers = [inputs.make_reduce_peer(p) for p in range(7)]
-    st = _requantize_local_case(fp4q, peers, inputs.make_reduce_peer(7), True, "reduce-k7+local")
-    _say("  %s" % st)
+    _say("requantize+local full k=7 4096x11008")
+    peers, trip = reduce_peers
+    ref = oracle.requantize(trip[:7], debug=True, local=peers[7])
+    out = fp4q.fp4q_reduce_requantize([tuple(to_dev(a) for a in t) for t in trip[:7]],
+                                      local=to_dev(peers[7]))
+    torch.cuda.synchronize()
+    _say("  %s" % parity.check_compress_exact([o.cpu().numpy() for o in out], ref))
 
 
 def test_two_exchange_allreduce_emulated(fp4q):
